@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+closed forms of the block format, exact dyadic arithmetic, a brute-force
+sort, library softmax, invariants of the plan, and an independent
+pure-Python implementation of the whole layer (tests/brute.py).
+
+The notes print no worked numeric example, so no value here comes from them;
+every expected value is computed in the test by other means.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import brute
+from oracle import moe_oracle as O
+from quantized_routed_expert_rl_amd import synth, workloads
+
+
+# ---------------------------------------------------------------- helpers
+def pack_tensor(codes, scales, d, qbits):
+    """Write a block-format tensor from explicit fields, byte by byte, at the
+    positions the format defines (independent of every other packer)."""
+    codes = np.asarray(codes, np.int64).reshape(-1)
+    nb = codes.size // 256
+    up = lambda n: -(-n // 256) * 256
+    q_end = nb * 64
+    hb_off = up(q_end) if qbits == 3 else None
+    s_off = up(hb_off + nb * 32) if qbits == 3 else up(q_end)
+    d_off = up(s_off + nb * 4)
+    buf = np.zeros(up(d_off + nb * 2), np.uint8)
+    for f, c in enumerate(codes):
+        b, j = divmod(f, 256)
+        buf[64 * b + j // 4] |= (int(c) & 3) << (2 * (j % 4))
+        if qbits == 3:
+            buf[hb_off + 32 * b + j // 8] |= ((int(c) >> 2) & 1) << (j % 8)
+    scales = np.asarray(scales, np.int64).reshape(nb, 8)
+    for b in range(nb):
+        for g in range(8):
+            buf[s_off + 4 * b + g // 2] |= int(scales[b, g]) << (4 * (g % 2))
+    dh = np.asarray(d, np.float16).reshape(nb)
+    buf[d_off:d_off + 2 * nb] = dh.view(np.uint8)
+    return buf
+
+
+def exact_weight(c, s, d, qbits):
+    if qbits == 2:
+        return Fraction(d) * (2 * s + 1) * (2 * c - 3) / 32
+    return Fraction(d) * (2 * s + 1) * (2 * c - 7) / 64
+
+
+# ---------------------------------------------------------- block format
+def test_byte_counts():
+    assert O.block_layout(512 * 2048, 2)["total"] == 286_720       # 70 B/block
+    assert O.block_layout(512 * 2048, 3)["total"] == 417_792       # 102 B/block
+    assert O.slot_bytes(2048, 512, 2) == 860_160
+    assert O.slot_bytes(2048, 512, 3) == 1_253_376
+    # tiny tensor: 64 blocks -> Q 4096, S 256, D 128 padded to 256
+    assert O.block_layout(64 * 256, 2)["total"] == 4096 + 256 + 256
+    for n, qb in [(64 * 256, 2), (512 * 2048, 2), (512 * 2048, 3)]:
+        assert O.block_layout(n, qb)["total"] == synth.tensor_nbytes(n, qb)
+
+
+@pytest.mark.parametrize("qbits", [2, 3])
+def test_closed_form_every_code_and_scale(qbits):
+    ncode = 1 << qbits
+    nb = 2                                     # 16 groups: every scale 0..15
+    scales = np.arange(16).reshape(nb, 8)
+    codes = np.array([(f * 7 + f // 32) % ncode for f in range(256 * nb)])
+    d = np.array([2.0 ** -5, 0.0419921875], np.float16)   # both exact in f16
+    w = O.dequantize(pack_tensor(codes, scales, d, qbits), 256 * nb, qbits)
+    for f in range(256 * nb):
+        b, j = divmod(f, 256)
+        want = exact_weight(int(codes[f]), int(scales[b, j // 32]), float(d[b]), qbits)
+        assert Fraction(float(w[f])) == want, f
+    # every weight is a float32 value (at most 19 significant bits)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def test_levels_are_the_stated_sets():
+    """d = 1 and s = 0 leave 16*w = level: the 2-bit set and the eight evenly
+    spaced 3-bit levels in [-1.75, 1.75]."""
+    w2 = O.dequantize(pack_tensor(np.arange(256) % 4, np.zeros((1, 8)), [1.0], 2), 256, 2)
+    assert sorted(set((16 * w2).tolist())) == [-1.5, -0.5, 0.5, 1.5]
+    w3 = O.dequantize(pack_tensor(np.arange(256) % 8, np.zeros((1, 8)), [1.0], 3), 256, 3)
+    assert sorted(set((16 * w3).tolist())) == np.linspace(-1.75, 1.75, 8).tolist()
+
+
+@pytest.mark.parametrize("qbits", [2, 3])
+def test_field_positions(qbits):
+    """Changing one code, one group scale or one block scale changes exactly
+    the weights the format assigns to it."""
+    rng = np.random.default_rng(1)
+    nb = 3
+    base_codes = np.full(256 * nb, 1)
+    base_scales = np.zeros((nb, 8), np.int64)
+    base_d = np.ones(nb, np.float16)
+    w0 = O.dequantize(pack_tensor(base_codes, base_scales, base_d, qbits), 256 * nb, qbits)
+    for _ in range(40):
+        f = int(rng.integers(256 * nb))
+        c = base_codes.copy()
+        c[f] = (1 << qbits) - 1
+        w = O.dequantize(pack_tensor(c, base_scales, base_d, qbits), 256 * nb, qbits)
+        assert np.flatnonzero(w != w0).tolist() == [f]
+    for b in range(nb):
+        for g in range(8):
+            s = base_scales.copy()
+            s[b, g] = 5
+            w = O.dequantize(pack_tensor(base_codes, s, base_d, qbits), 256 * nb, qbits)
+            idx = np.flatnonzero(w != w0)
+            assert idx.tolist() == list(range(256 * b + 32 * g, 256 * b + 32 * g + 32))
+            assert np.allclose(w[idx], 11 * w0[idx])
+        dd = base_d.copy()
+        dd[b] = 3.0
+        w = O.dequantize(pack_tensor(base_codes, base_scales, dd, qbits), 256 * nb, qbits)
+        assert np.flatnonzero(w != w0).tolist() == list(range(256 * b, 256 * b + 256))
+
+
+def test_expert_matrices_split_and_orientation():
+    H, F = 256, 64
+    n = H * F
+    tb = O.block_layout(n, 2)["total"]
+    # gate: d=1, up: d=2, down: d=4, all codes 3 and scales 0 -> w = 1.5/16*d
+    parts = [pack_tensor(np.full(n, 3), np.zeros((n // 256, 8)), np.full(n // 256, dv), 2)
+             for dv in (1.0, 2.0, 4.0)]
+    slot = np.concatenate(parts)
+    assert slot.size == 3 * tb
+    wg, wu, wd = O.expert_matrices(slot, H, F, 2)
+    assert wg.shape == (F, H) and wu.shape == (F, H) and wd.shape == (H, F)
+    assert np.all(wg == 1.5 / 16) and np.all(wu == 3.0 / 16) and np.all(wd == 6.0 / 16)
+
+
+# ---------------------------------------------------------------- router
+def test_logits_one_hot_columns_and_bias():
+    rng = np.random.default_rng(2)
+    E, H = 24, 256
+    W = rng.standard_normal((E, H)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    for i in [0, 7, 255]:
+        x = np.zeros(H, np.float32)
+        x[i] = 1.0
+        assert np.array_equal(O.router_logits(x, W, None)[0], W[:, i])
+        assert np.array_equal(O.router_logits(x, W, b)[0],
+                              (W[:, i].astype(np.float64) + b).astype(np.float32))
+    assert np.array_equal(O.router_logits(np.zeros(H, np.float32), W, b)[0], b)
+
+
+def test_logits_dyadic_exact():
+    """With W in 2^-10 Z (|num| <= 64) and x in 2^-6 Z (|num| <= 128), H=2048,
+    every partial sum is exact, so the logit equals the integer sum exactly."""
+    rng = np.random.default_rng(3)
+    E, H = 32, 2048
+    nw = rng.integers(-64, 65, (E, H))
+    nx = rng.integers(-128, 129, (3, H))
+    W = (nw / 1024.0).astype(np.float32)
+    x = (nx / 64.0).astype(np.float32)
+    got = O.router_logits(x, W, None)
+    for t in range(3):
+        for e in range(E):
+            exact = Fraction(int(np.dot(nw[e], nx[t])), 1 << 16)
+            assert Fraction(float(got[t, e])) == exact
+
+
+# ------------------------------------------------------------- selection
+def brute_select(row, k):
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_matches_full_sort(seed):
+    rng = np.random.default_rng(seed)
+    E, k = 64, 10
+    rows = [rng.standard_normal(E).astype(np.float32),
+            rng.integers(-3, 4, E).astype(np.float32),           # many ties
+            np.where(rng.random(E) < 0.5, -0.0, 0.0).astype(np.float32)]  # +-0
+    for row in rows:
+        assert O.select_experts(row, k) == brute_select(row, k)
+
+
+def test_selection_ties_and_zero_input():
+    assert O.select_experts(np.zeros(512, np.float32), 10) == list(range(10))
+    W = np.random.default_rng(4).standard_normal((16, 32)).astype(np.float32)
+    W[9] = W[3]                       # duplicate router rows: exact ties
+    x = np.random.default_rng(5).standard_normal(32).astype(np.float32)
+    lg = O.router_logits(x, W, None)[0]
+    ids = O.select_experts(lg, 16)
+    assert ids.index(3) + 1 == ids.index(9)
+
+
+def test_selection_monotone_under_softmax():
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        row = rng.standard_normal(512).astype(np.float32) * 3
+        p = scipy.special.softmax(row.astype(np.float64))
+        by_p = sorted(range(512), key=lambda e: (-p[e], e))[:10]
+        assert O.select_experts(row, 10) == by_p
+
+
+# --------------------------------------------------------------- weights
+def test_weights_sum_and_special_cases():
+    rng = np.random.default_rng(7)
+    for k in (1, 2, 10, 32):
+        row = (rng.standard_normal(512) * 2).astype(np.float32)
+        ids = O.select_experts(row, k)
+        w = O.renormalized_weights(row, ids)
+        assert abs(float(w.astype(np.float64).sum()) - 1.0) <= k * 2.0 ** -24
+        full = scipy.special.softmax(row.astype(np.float64))[ids]
+        assert np.allclose(w, full / full.sum(), rtol=2 ** -23, atol=0)
+        # adding a constant to every logit changes nothing (on a 2^-10 grid
+        # the shift is exact, so the weights are bit-identical)
+        grid = (np.round(row.astype(np.float64) * 1024) / 1024).astype(np.float32)
+        wg = O.renormalized_weights(grid, ids)
+        w2 = O.renormalized_weights(grid + np.float32(4.0), ids)
+        assert np.array_equal(w2, wg)
+    assert O.renormalized_weights(np.float32([0.3, 2.0]), [1]).tolist() == [1.0]
+    for k in (1, 2, 4, 8):
+        w = O.renormalized_weights(np.zeros(16, np.float32), list(range(k)))
+        assert np.all(w == np.float32(1.0 / k))
+
+
+# ------------------------------------------------- lookup, miss and flag
+def test_lookup_miss_and_flag():
+    rng = np.random.default_rng(8)
+    E, H, k, T = 32, 256, 4, 5
+    W = rng.standard_normal((E, H)).astype(np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    table = rng.permutation(E).astype(np.int32)
+    r = O.route(x, W, None, table, k)
+    assert r.miss_count == 0 and r.early_out == 0
+    assert np.array_equal(r.slots, table[r.ids])
+    r = O.route(x, W, None, np.full(E, -1, np.int32), k)
+    assert r.miss_count == T * k and r.early_out == 1
+    hole = table.copy()
+    victim = int(r.ids[0, 2])
+    hole[victim] = -1
+    r = O.route(x, W, None, hole, k)
+    assert r.miss_count == int((r.ids == victim).sum()) and r.early_out == 1
+
+
+# ------------------------------------------------------ expert and sum
+def test_silu_special_values():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert O.silu(np.array([800.0]))[0] == 800.0
+    assert O.silu(np.array([-800.0]))[0] == 0.0
+    g = np.linspace(-20, 20, 401)
+    assert np.allclose(O.silu(g), g * scipy.special.expit(g), rtol=1e-15, atol=1e-300)
+
+
+def test_expert_one_hot_and_zero():
+    w = workloads.get("tiny")
+    slot = synth.expert_slot(w, 0, 3)
+    wg, wu, wd = O.expert_matrices(slot, w.hidden, w.width, 2)
+    for i in (0, 100, 255):
+        x = np.zeros((1, w.hidden), np.float32)
+        x[0, i] = 1.0
+        h, e = O.expert_forward(x, wg, wu, wd)
+        g, u = wg[:, i], wu[:, i]
+        assert np.array_equal(h[0], (g / (1 + np.exp(-g)) * u).astype(np.float32))
+        assert np.array_equal(e[0], (wd @ h[0].astype(np.float64)).astype(np.float32))
+    h, e = O.expert_forward(np.zeros((1, w.hidden), np.float32), wg, wu, wd)
+    assert not h.any() and not e.any()
+
+
+def test_ordered_sum_cancellation_and_single():
+    e = [np.float32([2.0 ** 24]), np.float32([1.0]), np.float32([-(2.0 ** 24)])]
+    assert O.ordered_sum(np.float32([1, 1, 1]), e)[0] == 1.0
+    v = np.random.default_rng(9).standard_normal(64).astype(np.float32)
+    assert np.array_equal(O.ordered_sum(np.float32([1.0]), [v]), v)
+
+
+# ------------------------------------------- independent brute force
+def _tiny_case(seed, H, E, k, F, T, qbits, bias):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(E)).astype(np.float32) if bias else None
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    table = rng.permutation(E).astype(np.int32)
+    n = H * F
+    pool = [np.concatenate([synth.random_tensor(rng, n, qbits) for _ in range(3)])
+            for _ in range(E)]
+    return W, b, x, table, pool
+
+
+CASES = [(s, H, E, k, F, T, qb, bias)
+         for s, (H, E, k, F, T, qb, bias) in enumerate([
+             (256, 16, 2, 64, 4, 2, False), (256, 8, 3, 32, 3, 3, True),
+             (512, 12, 4, 64, 2, 2, True), (256, 10, 1, 256, 2, 3, False),
+             (256, 6, 6, 32, 2, 2, False), (512, 9, 2, 96, 2, 2, True)])]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_oracle_vs_brute_force(case):
+    seed, H, E, k, F, T, qbits, bias = case
+    W, b, x, table, pool = _tiny_case(*case)
+    shape = O.LayerShape(H, E, k, F, qbits)
+    r, plan, y = O.prefill_chunk(shape, x, W, b, table, lambda s: pool[s], plan_cap=E)
+    ref = brute.layer(x, W, b, table, lambda s: pool[s].tobytes(), H, E, k, F, qbits)
+    assert r.ids.tolist() == ref["ids"]
+    assert np.allclose(r.logits, np.float32(ref["logits"]), rtol=2 ** -23, atol=0)
+    assert np.allclose(r.weights, np.float32(ref["weights"]), rtol=2 ** -22, atol=0)
+    assert np.allclose(y, ref["y"], rtol=1e-6, atol=1e-7)
+
+
+def test_tiny_workload_vs_brute_force():
+    w = workloads.get("tiny")
+    table = synth.residency(w)
+    pool = synth.build_pool(w, table)
+    x = synth.activations(w, w.tokens)
+    W = synth.router_weights(w, 0)
+    shape = O.LayerShape(w.hidden, w.n_experts, w.top_k, w.width, w.qbits)
+    r, _, y = O.prefill_chunk(shape, x, W, None, table[0], lambda s: pool[s], 512)
+    ref = brute.layer(x, W, None, table[0], lambda s: pool[s].tobytes(),
+                      w.hidden, w.n_experts, w.top_k, w.width, w.qbits)
+    assert r.ids.tolist() == ref["ids"]
+    assert np.allclose(y, ref["y"], rtol=1e-6, atol=1e-7)
+
+
+def test_brute_force_flags_a_miss():
+    W, b, x, table, pool = _tiny_case(*CASES[0])
+    r = O.route(x, W, b, table, 2)
+    table[r.ids[1, 0]] = -1
+    ref = brute.layer(x, W, b, table, None, 256, 16, 2, 64, 2)
+    r2 = O.route(x, W, b, table, 2)
+    assert ref["miss"] == r2.miss_count > 0 and "y" not in ref
+
+
+# ------------------------------------------------------- decode/prefill
+def test_prefill_rows_equal_decode_calls():
+    W, b, x, table, pool = _tiny_case(*CASES[2])
+    shape = O.LayerShape(512, 12, 4, 64, 2)
+    _, _, y = O.prefill_chunk(shape, x, W, b, table, lambda s: pool[s], plan_cap=4)
+    for t in range(x.shape[0]):
+        _, yd, _ = O.decode_layer(shape, x[t], W, b, table, lambda s: pool[s])
+        assert np.array_equal(y[t], yd)
+
+
+def test_early_out_produces_nothing():
+    W, b, x, table, pool = _tiny_case(*CASES[0])
+    shape = O.LayerShape(256, 16, 2, 64, 2)
+    r, y, h = O.decode_layer(shape, x[0], W, b, np.full(16, -1, np.int32), None)
+    assert r.early_out == 1 and y is None and h is None
+    r, plan, y = O.prefill_chunk(shape, x, W, b, np.full(16, -1, np.int32), None, 16)
+    assert r.early_out == 1 and plan is None and y is None
+
+
+# ------------------------------------------------------------------ plan
+def _check_plan(ids, E, cap, plan):
+    T, k = ids.shape
+    gb = plan.group_bounds.tolist()
+    assert gb[0] == 0 and gb[-1] == T and all(a < b for a, b in zip(gb, gb[1:]))
+    for a, b in zip(gb, gb[1:]):
+        union = set(ids[a:b].reshape(-1).tolist())
+        assert len(union) <= cap
+        if b < T:
+            assert len(union | set(ids[b].tolist())) > cap   # greedy: maximal
+    assert sorted(plan.pairs.tolist()) == list(range(T * k))
+    flat = ids.reshape(-1)
+    for g, (a, b) in enumerate(zip(gb, gb[1:])):
+        want = sorted(range(a * k, b * k), key=lambda p: (int(flat[p]), p))
+        assert plan.pairs[a * k:b * k].tolist() == want
+        bs, be = plan.group_bucket_start[g], plan.group_bucket_start[g + 1]
+        experts = plan.bucket_expert[bs:be].tolist()
+        assert experts == sorted(set(flat[a * k:b * k].tolist()))
+        for i in range(bs, be):
+            seg = plan.pairs[plan.bucket_start[i]:plan.bucket_start[i + 1]]
+            assert all(int(flat[p]) == plan.bucket_expert[i] for p in seg)
+            assert len(seg) == int((flat[a * k:b * k] == plan.bucket_expert[i]).sum())
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("cap", [3, 6, 12, 64])
+def test_pair_plan_invariants(seed, cap):
+    rng = np.random.default_rng(seed)
+    E, k, T = 40, 3, 37
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    plan = O.pair_plan(ids, E, cap)
+    _check_plan(ids, E, cap, plan)
+    if cap >= E:
+        assert plan.group_bounds.tolist() == [0, T]
+    if cap == k:
+        assert all(len(set(ids[a:b].reshape(-1).tolist())) <= k
+                   for a, b in zip(plan.group_bounds, plan.group_bounds[1:]))
+
+
+# --------------------------------------------------------------- stacks
+def test_rmsnorm_closed_form():
+    for c in (1.0, -3.0, 1e-3):
+        x = np.full((1, 64), c, np.float32)
+        want = np.float32(c / np.sqrt(c * c + 1e-6))
+        assert np.allclose(O.rmsnorm(x), want, rtol=2 ** -23, atol=0)
+    x = np.random.default_rng(10).standard_normal((3, 2048)).astype(np.float32) * 7
+    a = O.rmsnorm(x).astype(np.float64)
+    assert np.allclose((a * a).mean(axis=1), 1.0, rtol=1e-6)
+
+
+def test_residual_skip_is_identity():
+    x = np.random.default_rng(11).standard_normal(32).astype(np.float32)
+    assert np.array_equal(O.residual_add(x, None), x)
