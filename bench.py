@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""MoE-layer tokens/s on one MI355X: single-token decode and 512-token
+prefill of one routed-expert layer at real shape (hidden 2048, 512 experts,
+top-10, width 512, 2-bit block weights), with the roofline fraction of each
+path's dominant kernel and the CPU oracle timed beside it.
+
+A step is 256 independent single-token decode calls (router, top-k, lookup,
+gate/up, down, ordered sum for each token) on seeded synthetic inputs already
+resident in HBM; the 256 calls of a step are captured once as a HIP graph and
+replayed.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+METRIC = "MoE-layer tokens/sec (decode, prefill@512) + % HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=256, help="decode calls per step")
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
+    return ap.parse_args()
+
+
+def event_ms(fn, stream, reps):
+    """Average milliseconds of fn() over reps calls bracketed by HIP events
+    recorded on the stream the kernels run on."""
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_rl_amd import binding as B
+    from quantized_routed_expert_rl_amd import synth, workloads
+    from quantized_routed_expert_rl_amd.device import DeviceModel, RouteBuffers, to_dev
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    lib = B.lib
+
+    # ------------------------------------------------------------ decode
+    w = workloads.get("decode_1l")
+    model = DeviceModel(w)
+    T = args.tokens
+    X = to_dev(synth.activations(w, T, stream=1))
+    Y = torch.empty(T, w.hidden, device="cuda")
+    rb = RouteBuffers.alloc(T, w.top_k, w.n_experts, with_logits=False)
+    outs = [B.route_out(rb.ids[t], rb.weights[t], rb.slots[t], rb.miss_count, rb.early_out)
+            for t in range(T)]
+    scratch = model.decode_scratch()
+    d = model.desc
+    xp = [X[t].data_ptr() for t in range(T)]
+    yp = [Y[t].data_ptr() for t in range(T)]
+    W0, res, pool = model.router[0].data_ptr(), model.residency.data_ptr(), model.pool.data_ptr()
+    sp, sb = scratch.data_ptr(), scratch.numel()
+
+    def decode_step():
+        st = torch.cuda.current_stream().cuda_stream
+        for t in range(T):
+            rc = lib.moe_decode_layer(C.byref(d), 0, xp[t], W0, None, res, pool,
+                                      C.byref(outs[t]), sp, sb, yp[t], st)
+            if rc:
+                raise B.RlError(f"moe_decode_layer {rc}")
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(args.warmup, 1)):
+            decode_step()
+    stream.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            decode_step()
+        for _ in range(args.warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    run = graph.replay if graph is not None else decode_step
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    decode_tps = T * args.steps / dt
+    assert int(rb.early_out.cpu()[0]) == 0 and torch.isfinite(Y).all()
+
+    # eager timing of the same step (host launch overhead included)
+    with torch.cuda.stream(stream):
+        eager_ms = event_ms(decode_step, stream, 3)
+
+    # dominant kernel: gate/up GEMVs + SwiGLU of the 10 selected experts, one
+    # launch per token, each token routed to its own experts above
+    def gateup_all():
+        st = torch.cuda.current_stream().cuda_stream
+        for t in range(T):
+            lib.rl_decode_stage(C.byref(d), 1, xp[t], pool, C.byref(outs[t]), sp, sb, None, st)
+
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        gateup_all()
+    with torch.cuda.graph(g2, stream=stream):
+        gateup_all()
+    g2.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        gu_ms = event_ms(g2.replay, stream, 5) / T
+    tb = B.rl_tensor_bytes(d)
+    gu_bytes = w.top_k * 2 * tb + w.hidden * 4 + w.top_k * w.width * 4
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    layer_bytes = w.top_k * 3 * tb + w.n_experts * w.hidden * 4 + 2 * w.hidden * 4
+
+    line = {
+        "metric": METRIC,
+        "value": round(decode_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_1l: single-token decode of one MoE layer, hidden 2048, "
+                        "512 experts all resident, top-10, width 512, 2-bit block weights; "
+                        f"{T} independent tokens per step, HIP-graph replay"
+                        + (" (eager)" if graph is None else ""),
+            "tokens_per_step": T,
+            "layer_bytes_per_token": layer_bytes,
+            "us_per_token": round(ms_per_step * 1e3 / T, 3),
+            "eager_us_per_token": round(eager_ms * 1e3 / T, 3),
+        },
+        "roofline": {
+            "kernel": "decode_gateup_kernel<2,64>",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+            "us_per_launch": round(gu_ms * 1e3, 3),
+        },
+    }
+
+    # ------------------------------------------------------------ prefill
+    if not args.no_prefill:
+        w3 = workloads.get("prefill_1l")
+        m3 = DeviceModel(w3)
+        T3 = 512
+        X3 = to_dev(synth.activations(w3, T3))
+        Y3 = torch.empty(T3, w3.hidden, device="cuda")
+        r3 = RouteBuffers.alloc(T3, w3.top_k, w3.n_experts, with_logits=False)
+        s3 = m3.prefill_scratch(T3)
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                m3.prefill(0, X3, w3.plan_cap, r3, s3, Y3)
+            stream.synchronize()
+            p_ms = event_ms(lambda: m3.prefill(0, X3, w3.plan_cap, r3, s3, Y3), stream,
+                            args.prefill_reps)
+            stage_ms = {}
+            for stg, name in [(1, "gateup"), (2, "down")]:
+                stage_ms[name] = event_ms(
+                    lambda: B.rl_prefill_stage(m3.desc, stg, 0, T3, w3.plan_cap, X3,
+                                               m3.residency, m3.pool, r3.c(), s3, s3.numel(),
+                                               Y3), stream, args.prefill_reps)
+        plan = m3.read_plan(s3, T3)
+        U = plan["n_buckets"]
+        tb3 = B.rl_tensor_bytes(m3.desc)
+        P = T3 * w3.top_k
+        gb = {"gateup": U * 2 * tb3 + T3 * w3.hidden * 4 + P * w3.width * 4,
+              "down": U * tb3 + P * w3.width * 4 + P * w3.hidden * 4}
+        dom = max(stage_ms, key=stage_ms.get)
+        ach = gb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        chunk_bytes = U * 3 * tb3 + w3.n_experts * w3.hidden * 4 + 2 * T3 * w3.hidden * 4
+        line["prefill"] = {
+            "value": round(T3 / (p_ms * 1e-3), 1),
+            "unit": "tokens/s",
+            "ms_per_chunk": round(p_ms, 4),
+            "config": {"workload": "prefill_1l: one 512-token chunk, 5120 pairs, plan cap 512, "
+                                   "same layer shape", "distinct_experts": U,
+                       "chunk_bytes": chunk_bytes,
+                       "chunk_frac_of_hbm": round(chunk_bytes / (p_ms * 1e-3) / 1e9
+                                                  / PEAK_HBM_GBS, 4)},
+            "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "roofline": {"kernel": f"prefill_{dom}_kernel", "bound": "hbm",
+                         "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": gb[dom]},
+        }
+
+    # -------------------------------------------------------- cpu oracle
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import moe_oracle as O
+        host_pool = synth.build_pool(w, model.table)
+        Wr = synth.router_weights(w, 0)
+        xs = synth.activations(w, T, stream=1)
+        shape = O.LayerShape(w.hidden, w.n_experts, w.top_k, w.width, w.qbits)
+        n = 0
+        t0 = time.perf_counter()
+        while n < T and (time.perf_counter() - t0 < args.cpu_seconds or n == 0):
+            O.decode_layer(shape, xs[n], Wr, None, model.table[0], lambda s: host_pool[s])
+            n += 1
+        cdt = time.perf_counter() - t0
+        blas = [i.get("num_threads", 1) for i in threadpool_info()]
+        line["cpu_baseline"] = {
+            "value": round(n / cdt, 3), "unit": "tokens/s", "cores": max(blas + [1]),
+            "kind": "oracle",
+            "sample": f"first {n} of the {T} decode_1l tokens through oracle.decode_layer "
+                      f"({cdt:.1f} s); float64 NumPy, BLAS threads {max(blas + [1])}, "
+                      f"host has {os.cpu_count()} logical CPUs"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * rl_moe.h -- C ABI of the routed mixture-of-experts FFN for AMD MI355X.
+ *
+ * One MoE layer of a Qwen3-Next-style decoder: router GEMV, softmax top-k
+ * selection, residency lookup with a per-layer early-out flag, block-quantised
+ * SwiGLU experts (gate/up, down) and a weighted sum of each token's experts in
+ * router rank order.  Two forms: single-token decode and chunked prefill over
+ * (expert, token) pairs sorted by expert.
+ *
+ * Sources (the Red Lite development notes):
+ *   dev21  "Red Lite dev21 - GPU-routed decode (full residency)", "What changed":
+ *          selection rule, renormalised weights, residency table, slot table,
+ *          per-layer miss count.
+ *   dev23  "Red Lite dev23 - per-layer early-out and pre-gated expert prefetch",
+ *          "What changed": every kernel of the layer returns at once when the
+ *          early-out flag is set.
+ *   dev20  "Red Lite dev20 - batched prompt ingestion", "What changed": chunks,
+ *          plans of at most 512 distinct experts split into consecutive token
+ *          groups past the cap, pairs sorted by expert, per-token sum in router
+ *          selection order.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
+ *     and owns every buffer and keeps it alive until the work queued on
+ *     `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it: no allocation, no free, no synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     negative return code means nothing was enqueued.  RL_E_DEVICE means a
+ *     launch failed (hipGetLastError) and the queued state is unspecified.
+ *   - The early-out flag is data, not an error.
+ *   - Calls on different streams must not share outputs or scratch.
+ *   - NaN or infinite inputs give unspecified (but in-bounds) results.
+ *
+ * Block format of an expert tensor (the workload's 2- and 3-bit format).
+ *   The R x C elements, row-major and flattened, form blocks of 256 values;
+ *   group g = 0..7 of a block holds 32 consecutive values.  Weight =
+ *   d * (2s+1)/16 * level(c): level = c - 1.5 (2-bit code c), or (c - 3.5)/2
+ *   (3-bit code).  Byte planes, each at a 256-byte aligned offset, in order:
+ *     Q   nb*64 B  low code bits: element j of block b at byte 64b + j/4,
+ *                  bits 2(j%4), 2(j%4)+1
+ *     Hb  nb*32 B  (3-bit only) code bit 2: byte 32b + j/8, bit j%8
+ *     S   nb*4  B  group scale s of group g: byte 4b + g/2, low nibble if g even
+ *     D   nb*2  B  block scale d, IEEE binary16 little endian, at byte 2b
+ *   and the tensor size is rounded up to 256 bytes (rl_tensor_bytes).
+ *   An expert slot is gate [F x H], up [F x H], down [H x F] back to back;
+ *   slot s of the pool starts at byte s * rl_slot_bytes().
+ */
+#ifndef RL_MOE_H
+#define RL_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Shape of one MoE layer (host struct).
+ * Supported: hidden in {256, 512, 1024, 2048}; width a power of two in
+ * [32, 2048]; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
+ * n_layers >= 1; qbits in {2, 3}; n_slots >= 0 (slots in the pool). */
+typedef struct rl_moe_desc {
+  int32_t hidden;     /* H */
+  int32_t n_experts;  /* E */
+  int32_t top_k;      /* k */
+  int32_t width;      /* F, expert intermediate width */
+  int32_t n_layers;   /* rows of the residency table */
+  int32_t qbits;      /* 2 or 3 */
+  int32_t n_slots;    /* slots in slot_pool; table entries >= n_slots miss */
+} rl_moe_desc;
+
+enum {
+  RL_OK = 0,
+  RL_E_INVAL = -1,    /* null required pointer or misaligned buffer */
+  RL_E_SHAPE = -2,    /* unsupported layer shape in the descriptor */
+  RL_E_RANGE = -3,    /* layer, n_tokens or plan_cap out of range */
+  RL_E_SCRATCH = -4,  /* scratch smaller than the size query returns */
+  RL_E_DEVICE = -5    /* a kernel launch failed */
+};
+
+/* Routing results of one call (host struct of device pointers).
+ * The notes' rl_route writes the slot table and weights the expert kernels
+ * read and a per-layer miss count (dev21, "What changed"). */
+typedef struct rl_route_out {
+  int32_t*  ids;        /* [T][k] expert ids in router rank order           */
+  float*    weights;    /* [T][k] softmax weights renormalised over the k   */
+  int32_t*  slots;      /* [T][k] residency[layer][id], -1 = not resident   */
+  uint32_t* miss_count; /* [1] selections with slot -1, over the T tokens  */
+  uint32_t* early_out;  /* [1] 1 when miss_count > 0, else 0 (overwritten)  */
+  float*    logits;     /* [T][E] router logits, or NULL = not stored       */
+} rl_route_out;
+
+/* Bytes of one expert tensor (F x H elements) and of one slot (3 tensors). */
+int64_t rl_tensor_bytes(const rl_moe_desc* d);
+int64_t rl_slot_bytes(const rl_moe_desc* d);
+
+/* Scratch sizes in bytes (negative = error code for a bad descriptor).
+ * Scratch must be 256-byte aligned and zero-filled before its first use;
+ * every call leaves its synchronisation words at zero again, so one zeroed
+ * buffer serves any number of calls on one stream. */
+int64_t rl_route_scratch_bytes(const rl_moe_desc* d, int32_t n_tokens);
+int64_t rl_decode_scratch_bytes(const rl_moe_desc* d);
+int64_t rl_prefill_scratch_bytes(const rl_moe_desc* d, int32_t max_tokens);
+
+/* Where moe_prefill_chunk keeps its plan inside scratch (byte offsets from
+ * the scratch base), so that callers and tests can read it after the call.
+ * The offsets depend on the call's token count: pass the n_tokens of the
+ * moe_prefill_chunk call as max_tokens here.
+ * All arrays are int32; they are written only when early_out is 0.
+ *   n_groups            [1]
+ *   group_bounds        [n_groups+1] token boundaries of the token groups
+ *   n_buckets           [1]   distinct (group, expert) buckets
+ *   group_bucket_start  [n_groups+1] first bucket of each group
+ *   bucket_expert       [n_buckets]  expert id of each bucket (ascending
+ *                                    inside a group)
+ *   bucket_start        [n_buckets+1] offsets into pairs
+ *   pairs               [T*k] pair ids p = t*k + r, per group sorted by
+ *                                    expert, then by p (stable) */
+typedef struct rl_prefill_layout {
+  int64_t n_groups, group_bounds, n_buckets, group_bucket_start,
+          bucket_expert, bucket_start, pairs, total;
+} rl_prefill_layout;
+int rl_prefill_plan_layout(const rl_moe_desc* d, int32_t max_tokens,
+                           rl_prefill_layout* out /* (host) */);
+
+const char* rl_strerror(int code);
+
+/* Router, softmax top-k, renormalised weights and residency lookup for
+ * n_tokens tokens of layer `layer` (dev21 "What changed"; dev23 "What
+ * changed" for the flag).
+ *   x          [T][H] float32 activations
+ *   router_w   [E][H] float32
+ *   router_bias[E] float32 or NULL
+ *   residency  [L][E] int32 slot indices; -1 = not resident.  Entries outside
+ *              [-1, n_slots) are treated as not resident.
+ *   out        (host) struct of device pointers; ids, weights, slots,
+ *              miss_count, early_out required, logits optional.
+ * Logits accumulate in float64 and round once to float32; experts are taken
+ * by logit, largest first, ties to the lower index (-0 == +0); weights are
+ * exp(l_r - l_0) / sum_j exp(l_j - l_0) over the k taken, summed in rank
+ * order.  The flag is overwritten on every call. */
+int rl_route(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
+             const float* x, const float* router_w, const float* router_bias,
+             const int32_t* residency, const rl_route_out* out,
+             void* scratch, int64_t scratch_bytes, void* stream);
+
+/* One single-token decode step of layer `layer`: rl_route for the token, then
+ * the k experts' gate/up GEMVs with SwiGLU, the down GEMVs, and
+ *   y = sum_{r=0..k-1} w_r * (W_down[slot_r] h_r)
+ * accumulated in rank order (fused multiply-add from 0).  When the router
+ * raises the flag every expert kernel returns at once and y is NOT written
+ * (dev23 "What changed").
+ *   x [H] float32; slot_pool: n_slots slots of rl_slot_bytes bytes;
+ *   route: where the routing results go (as for rl_route);
+ *   scratch: rl_decode_scratch_bytes bytes; y [H] float32. */
+int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x,
+                     const float* router_w, const float* router_bias,
+                     const int32_t* residency, const void* slot_pool,
+                     const rl_route_out* route, void* scratch,
+                     int64_t scratch_bytes, float* y, void* stream);
+
+/* One prefill chunk of n_tokens tokens through layer `layer` (dev20 "What
+ * changed"): route every token, build the chunk's plan -- consecutive token
+ * groups whose union of selected experts stays within plan_cap (a token
+ * joins the current group unless the union would exceed the cap), and per
+ * group the (expert, token) pairs sorted by expert -- run the batched
+ * gate/up and down projections over the pairs and sum each token's k expert
+ * outputs in rank order.  One miss anywhere in the chunk raises the chunk's
+ * flag; then nothing after routing runs and y is NOT written.
+ *   x [T][H]; y [T][H] float32; plan_cap >= top_k;
+ *   scratch: rl_prefill_scratch_bytes(d, max_tokens) with max_tokens >= T. */
+int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
+                      int32_t plan_cap, const float* x, const float* router_w,
+                      const float* router_bias, const int32_t* residency,
+                      const void* slot_pool, const rl_route_out* route,
+                      void* scratch, int64_t scratch_bytes, float* y,
+                      void* stream);
+
+/* Stage entry points, for tests and benchmarks: each enqueues exactly one
+ * kernel of a path above, with the same arguments and scratch layout.
+ *   rl_decode_stage: stage 1 = gate/up GEMVs + SwiGLU of the k selected
+ *     experts (needs `route` filled by rl_route for this token; h goes to
+ *     scratch); stage 2 = down GEMVs + rank-ordered sum into y (needs stage 1
+ *     in the same scratch).  Same early-out behaviour as moe_decode_layer.
+ *   rl_prefill_stage: stage 0 = plan (needs `route` filled by rl_route for
+ *     the n_tokens tokens of x), 1 = batched gate/up, 2 = batched down,
+ *     3 = per-token ordered sum into y; each stage needs the previous ones in
+ *     the same scratch (sized for n_tokens).
+ * Sources as for moe_decode_layer (dev21, dev23) and moe_prefill_chunk (dev20). */
+int rl_decode_stage(const rl_moe_desc* d, int32_t stage, const float* x,
+                    const void* slot_pool, const rl_route_out* route,
+                    void* scratch, int64_t scratch_bytes, float* y, void* stream);
+int rl_prefill_stage(const rl_moe_desc* d, int32_t stage, int32_t layer,
+                     int32_t n_tokens, int32_t plan_cap, const float* x,
+                     const int32_t* residency, const void* slot_pool,
+                     const rl_route_out* route, void* scratch,
+                     int64_t scratch_bytes, float* y, void* stream);
+
+/* Helpers for stacks of layers (not part of the MoE layer itself).
+ * rl_rmsnorm: out[t] = x[t] / sqrt(mean(x[t]^2) + eps), no weight.
+ * rl_residual_add: x[t] += y[t], skipped entirely when *early_out != 0
+ * (early_out may be NULL = always add).  hidden must be a multiple of 256. */
+int rl_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, float* out,
+               float eps, void* stream);
+int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
+                    const uint32_t* early_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RL_MOE_H */

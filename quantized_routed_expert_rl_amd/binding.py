@@ -1,0 +1,197 @@
+"""ctypes binding of librlmoe (include/rl_moe.h): argument marshalling only.
+
+Every function keeps the C name and argument order.  Device buffers are
+torch tensors on the ROCm device (their ``data_ptr()`` is passed); ``stream``
+defaults to torch's current stream.  Nothing here computes any part of the
+MoE layer: if the shared library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librlmoe.so")
+
+RL_OK, RL_E_INVAL, RL_E_SHAPE, RL_E_RANGE, RL_E_SCRATCH, RL_E_DEVICE = 0, -1, -2, -3, -4, -5
+
+
+class RlMoeDesc(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("width", C.c_int32), ("n_layers", C.c_int32), ("qbits", C.c_int32),
+                ("n_slots", C.c_int32)]
+
+
+class RlRouteOut(C.Structure):
+    _fields_ = [("ids", C.c_void_p), ("weights", C.c_void_p), ("slots", C.c_void_p),
+                ("miss_count", C.c_void_p), ("early_out", C.c_void_p), ("logits", C.c_void_p)]
+
+
+class RlPrefillLayout(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("n_groups", "group_bounds", "n_buckets",
+                                          "group_bucket_start", "bucket_expert",
+                                          "bucket_start", "pairs", "total")]
+
+
+# exported symbol -> (restype, argtypes)
+_SIGS = {
+    "rl_tensor_bytes": (C.c_int64, [C.POINTER(RlMoeDesc)]),
+    "rl_slot_bytes": (C.c_int64, [C.POINTER(RlMoeDesc)]),
+    "rl_route_scratch_bytes": (C.c_int64, [C.POINTER(RlMoeDesc), C.c_int32]),
+    "rl_decode_scratch_bytes": (C.c_int64, [C.POINTER(RlMoeDesc)]),
+    "rl_prefill_scratch_bytes": (C.c_int64, [C.POINTER(RlMoeDesc), C.c_int32]),
+    "rl_prefill_plan_layout": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32,
+                                         C.POINTER(RlPrefillLayout)]),
+    "rl_strerror": (C.c_char_p, [C.c_int]),
+    "rl_route": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                           C.c_void_p, C.c_void_p, C.POINTER(RlRouteOut), C.c_void_p,
+                           C.c_int64, C.c_void_p]),
+    "moe_decode_layer": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RlRouteOut),
+                                   C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "moe_prefill_chunk": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
+                                    C.c_void_p]),
+    "rl_decode_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p, C.c_void_p,
+                                  C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
+                                  C.c_void_p]),
+    "rl_prefill_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
+                                   C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
+                                   C.c_void_p]),
+    "rl_rmsnorm": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_float,
+                             C.c_void_p]),
+    "rl_residual_add": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p]),
+}
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_routed_expert_rl_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class RlError(RuntimeError):
+    pass
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def check(rc: int, what: str = "") -> int:
+    if rc < 0:
+        raise RlError(f"{what}: {lib.rl_strerror(int(rc)).decode()} ({rc})")
+    return rc
+
+
+def desc(hidden, n_experts, top_k, width, n_layers=1, qbits=2, n_slots=0) -> RlMoeDesc:
+    return RlMoeDesc(hidden, n_experts, top_k, width, n_layers, qbits, n_slots)
+
+
+def route_out(ids, weights, slots, miss_count, early_out, logits=None) -> RlRouteOut:
+    return RlRouteOut(_ptr(ids), _ptr(weights), _ptr(slots), _ptr(miss_count),
+                      _ptr(early_out), _ptr(logits))
+
+
+# ----------------------------------------------------------- size queries
+def rl_tensor_bytes(d: RlMoeDesc) -> int:
+    return check(lib.rl_tensor_bytes(C.byref(d)), "rl_tensor_bytes")
+
+
+def rl_slot_bytes(d: RlMoeDesc) -> int:
+    return check(lib.rl_slot_bytes(C.byref(d)), "rl_slot_bytes")
+
+
+def rl_route_scratch_bytes(d: RlMoeDesc, n_tokens: int) -> int:
+    return check(lib.rl_route_scratch_bytes(C.byref(d), n_tokens), "rl_route_scratch_bytes")
+
+
+def rl_decode_scratch_bytes(d: RlMoeDesc) -> int:
+    return check(lib.rl_decode_scratch_bytes(C.byref(d)), "rl_decode_scratch_bytes")
+
+
+def rl_prefill_scratch_bytes(d: RlMoeDesc, max_tokens: int) -> int:
+    return check(lib.rl_prefill_scratch_bytes(C.byref(d), max_tokens),
+                 "rl_prefill_scratch_bytes")
+
+
+def rl_prefill_plan_layout(d: RlMoeDesc, max_tokens: int) -> RlPrefillLayout:
+    out = RlPrefillLayout()
+    check(lib.rl_prefill_plan_layout(C.byref(d), max_tokens, C.byref(out)),
+          "rl_prefill_plan_layout")
+    return out
+
+
+# ------------------------------------------------------------- hot path
+def rl_route(d, layer, n_tokens, x, router_w, router_bias, residency, out: RlRouteOut,
+             scratch, scratch_bytes, stream=None) -> int:
+    return check(lib.rl_route(C.byref(d), layer, n_tokens, _ptr(x), _ptr(router_w),
+                              _ptr(router_bias), _ptr(residency), C.byref(out), _ptr(scratch),
+                              scratch_bytes, _stream(stream)), "rl_route")
+
+
+def moe_decode_layer(d, layer, x, router_w, router_bias, residency, slot_pool,
+                     route: RlRouteOut, scratch, scratch_bytes, y, stream=None) -> int:
+    return check(lib.moe_decode_layer(C.byref(d), layer, _ptr(x), _ptr(router_w),
+                                      _ptr(router_bias), _ptr(residency), _ptr(slot_pool),
+                                      C.byref(route), _ptr(scratch), scratch_bytes, _ptr(y),
+                                      _stream(stream)), "moe_decode_layer")
+
+
+def moe_prefill_chunk(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,
+                      slot_pool, route: RlRouteOut, scratch, scratch_bytes, y,
+                      stream=None) -> int:
+    return check(lib.moe_prefill_chunk(C.byref(d), layer, n_tokens, plan_cap, _ptr(x),
+                                       _ptr(router_w), _ptr(router_bias), _ptr(residency),
+                                       _ptr(slot_pool), C.byref(route), _ptr(scratch),
+                                       scratch_bytes, _ptr(y), _stream(stream)),
+                 "moe_prefill_chunk")
+
+
+def rl_decode_stage(d, stage, x, slot_pool, route: RlRouteOut, scratch, scratch_bytes, y,
+                    stream=None) -> int:
+    return check(lib.rl_decode_stage(C.byref(d), stage, _ptr(x), _ptr(slot_pool), C.byref(route),
+                                     _ptr(scratch), scratch_bytes, _ptr(y), _stream(stream)),
+                 "rl_decode_stage")
+
+
+def rl_prefill_stage(d, stage, layer, n_tokens, plan_cap, x, residency, slot_pool,
+                     route: RlRouteOut, scratch, scratch_bytes, y, stream=None) -> int:
+    return check(lib.rl_prefill_stage(C.byref(d), stage, layer, n_tokens, plan_cap, _ptr(x),
+                                      _ptr(residency), _ptr(slot_pool), C.byref(route),
+                                      _ptr(scratch), scratch_bytes, _ptr(y), _stream(stream)),
+                 "rl_prefill_stage")
+
+
+def rl_rmsnorm(n_tokens, hidden, x, out, eps=1e-6, stream=None) -> int:
+    return check(lib.rl_rmsnorm(n_tokens, hidden, _ptr(x), _ptr(out), eps, _stream(stream)),
+                 "rl_rmsnorm")
+
+
+def rl_residual_add(n_tokens, hidden, x, y, early_out=None, stream=None) -> int:
+    return check(lib.rl_residual_add(n_tokens, hidden, _ptr(x), _ptr(y), _ptr(early_out),
+                                     _stream(stream)), "rl_residual_add")

@@ -1,0 +1,81 @@
+// Launch interfaces between the C ABI (abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rl_common.h"
+
+namespace rl {
+
+struct RouteArgs {
+  const float* x;
+  const float* W;
+  const float* bias;
+  int T, E, H, k, layer, n_slots;
+  const int32_t* residency;
+  float* logits;       // [T][E] scratch
+  float* logits_out;   // optional copy for the caller
+  uint32_t* counter;   // T == 1 only: zeroed scratch word, left at zero
+  int32_t* ids;
+  float* weights;
+  int32_t* slots;
+  uint32_t* miss_count;
+  uint32_t* early_out;
+};
+void launch_route(const RouteArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  PoolView pool;
+  int H, F, k, qbits;
+  const float* x;
+  const int32_t* slots;
+  const float* weights;
+  const uint32_t* early_out;
+  float* hbuf;         // [k][F] scratch
+  float* y;
+};
+void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);
+void launch_decode_down_sum(const DecodeArgs& a, hipStream_t st);
+
+// Plan of a prefill chunk inside scratch (see rl_prefill_layout).
+struct PlanPtrs {
+  int32_t* n_groups;
+  int32_t* group_bounds;
+  int32_t* n_buckets;
+  int32_t* group_bucket_start;
+  int32_t* bucket_expert;
+  int32_t* bucket_start;
+  int32_t* pairs;
+  // internal
+  int32_t* counts;        // [max_groups*E]
+  int32_t* offs;          // [max_groups*E]
+  int32_t* bucket_slot;   // [T*k]
+  int32_t* tile_start;    // [T*k+1] token tiles before each bucket
+  int32_t* n_tiles;       // [1]
+};
+
+struct PrefillArgs {
+  PoolView pool;
+  int T, H, F, E, k, qbits, plan_cap, layer;
+  const float* x;
+  const int32_t* residency;
+  const int32_t* ids;
+  const int32_t* slots;
+  const float* weights;
+  const uint32_t* early_out;
+  PlanPtrs plan;
+  float* hbuf;   // [T*k][F], rows in sorted pair order
+  float* ebuf;   // [T*k][H], rows by pair id p = t*k + r
+  float* y;
+};
+void launch_prefill_plan(const PrefillArgs& a, hipStream_t st);
+void launch_prefill_gateup(const PrefillArgs& a, hipStream_t st);
+void launch_prefill_down(const PrefillArgs& a, hipStream_t st);
+void launch_prefill_sum(const PrefillArgs& a, hipStream_t st);
+
+void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st);
+void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,
+                         hipStream_t st);
+
+}  // namespace rl

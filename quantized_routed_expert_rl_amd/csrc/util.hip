@@ -1,0 +1,51 @@
+// Helpers for stacks of MoE layers: weightless RMSNorm before each layer and
+// the residual add after it, skipped when the layer's early-out flag is set.
+// They are not part of the MoE layer; they let a stack of layers run on the
+// device without host round trips.
+#include "rl_common.h"
+#include "rl_kernels.h"
+
+namespace rl {
+
+// One block per token: out = x / sqrt(mean(x^2) + eps), the mean of squares
+// accumulated in float64.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* __restrict__ x,
+                                                      float* __restrict__ out, float eps) {
+  const int64_t base = int64_t(blockIdx.x) * H;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const double v = x[base + i];
+    s = fma(v, v, s);
+  }
+  s = wave_sum_f64(s);
+  __shared__ double s_w[4];
+  __shared__ double s_inv;
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) s_inv = 1.0 / sqrt((s_w[0] + s_w[1] + s_w[2] + s_w[3]) / H + double(eps));
+  __syncthreads();
+  const double inv = s_inv;
+  for (int i = threadIdx.x; i < H; i += 256) out[base + i] = float(double(x[base + i]) * inv);
+}
+
+__global__ __launch_bounds__(256) void residual_add_kernel(int64_t n, float* __restrict__ x,
+                                                           const float* __restrict__ y,
+                                                           const uint32_t* __restrict__ early_out) {
+  if (early_out && *early_out) return;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    x[i] = x[i] + y[i];
+}
+
+void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st) {
+  rmsnorm_kernel<<<T, 256, 0, st>>>(H, x, out, eps);
+}
+
+void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,
+                         hipStream_t st) {
+  const int64_t n = int64_t(T) * H;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  residual_add_kernel<<<int(blocks), 256, 0, st>>>(n, x, y, early_out);
+}
+
+}  // namespace rl

@@ -1,0 +1,151 @@
+"""Parity of moe_prefill_chunk with the CPU oracle on the GPU: routing and the
+plan exactly, y within tolerance; prefill rows against single-token decode."""
+import numpy as np
+import pytest
+import torch
+
+from gpu.common import check_route, close, oracle_route, shape_of
+from oracle import moe_oracle as O
+from quantized_routed_expert_rl_amd import binding as B
+from quantized_routed_expert_rl_amd import synth, workloads
+from quantized_routed_expert_rl_amd.device import DeviceModel, RouteBuffers, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return DeviceModel(workloads.get("tiny"))
+
+
+@pytest.fixture(scope="module")
+def real():
+    return DeviceModel(workloads.get("prefill_1l"))
+
+
+def run_chunk(model, x, plan_cap, layer=0, max_tokens=None):
+    w = model.w
+    T = x.shape[0]
+    max_tokens = max_tokens or T
+    scratch = model.prefill_scratch(max_tokens)
+    out = RouteBuffers.alloc(T, w.top_k, w.n_experts)
+    y = torch.full((T, w.hidden), float("nan"), device="cuda")
+    model.prefill(layer, to_dev(x), plan_cap, out, scratch, y)
+    torch.cuda.synchronize()
+    return out, y, scratch
+
+
+def check_plan(model, scratch, max_tokens, ref_plan, T, k):
+    got = model.read_plan(scratch, max_tokens)
+    assert got["n_groups"] == len(ref_plan.group_bounds) - 1
+    assert np.array_equal(got["group_bounds"], ref_plan.group_bounds)
+    assert got["n_buckets"] == len(ref_plan.bucket_expert)
+    assert np.array_equal(got["group_bucket_start"], ref_plan.group_bucket_start)
+    assert np.array_equal(got["bucket_expert"], ref_plan.bucket_expert)
+    assert np.array_equal(got["bucket_start"], ref_plan.bucket_start)
+    assert np.array_equal(got["pairs"](T * k), ref_plan.pairs)
+
+
+@pytest.mark.parametrize("plan_cap", [16, 2, 3, 5])
+def test_prefill_tiny(tiny, plan_cap):
+    w = tiny.w
+    x = synth.activations(w, w.tokens)
+    out, y, scratch = run_chunk(tiny, x, plan_cap)
+    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, tiny.router[0].cpu().numpy(), None,
+                                     tiny.table[0], tiny.read_slot, plan_cap)
+    check_route(out, r)
+    check_plan(tiny, scratch, w.tokens, plan, w.tokens, w.top_k)
+    close(y.cpu().numpy(), y_ref, "y")
+
+
+@pytest.mark.parametrize("T,plan_cap", [(37, 16), (64, 4), (200, 7), (1, 2)])
+def test_prefill_tiny_ragged(tiny, T, plan_cap):
+    w = tiny.w
+    x = synth.activations(w, T, stream=T)
+    out, y, scratch = run_chunk(tiny, x, plan_cap, max_tokens=T + 5)
+    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, tiny.router[0].cpu().numpy(), None,
+                                     tiny.table[0], tiny.read_slot, plan_cap)
+    check_route(out, r)
+    check_plan(tiny, scratch, T, plan, T, w.top_k)      # plan layout of a T-token call
+    close(y.cpu().numpy(), y_ref, "y")
+
+
+def test_prefill_real_chunk_sampled(real):
+    """A 512-token chunk at real shape: every id, slot and the whole plan exact;
+    y of 12 sampled tokens against the oracle."""
+    w = real.w
+    x = synth.activations(w, 512)
+    out, y, scratch = run_chunk(real, x, 512)
+    sample = [0, 1, 2, 100, 255, 256, 300, 411, 500, 509, 510, 511]
+    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, real.router[0].cpu().numpy(), None,
+                                     real.table[0], real.read_slot, 512, tokens=sample)
+    check_route(out, r)
+    check_plan(real, scratch, 512, plan, 512, w.top_k)
+    yg = y.cpu().numpy()
+    close(yg[sample], y_ref[sample], "y sample")
+    assert not np.isnan(yg).any()
+
+
+def test_prefill_plan_cap_and_chunk_invariance(real):
+    """y does not depend on the plan cap nor on how the prompt is chunked."""
+    w = real.w
+    x = synth.activations(w, 96, stream=3)
+    _, y_full, _ = run_chunk(real, x, 512)
+    _, y_cap, _ = run_chunk(real, x, 40)
+    close(y_cap.cpu().numpy(), y_full.cpu().numpy(), "cap 40 vs 512")
+    parts = [run_chunk(real, x[a:b], 512)[1] for a, b in [(0, 32), (32, 33), (33, 96)]]
+    close(torch.cat(parts).cpu().numpy(), y_full.cpu().numpy(), "chunks 32/1/63")
+
+
+def test_prefill_equals_decode(real):
+    w = real.w
+    x = synth.activations(w, 24, stream=5)
+    out, y, _ = run_chunk(real, x, 512)
+    scratch = real.decode_scratch()
+    for t in range(24):
+        o1 = RouteBuffers.alloc(1, w.top_k, w.n_experts)
+        y1 = torch.empty(w.hidden, device="cuda")
+        real.decode(0, to_dev(x[t:t + 1]), o1, scratch, y1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.ids[0], out.ids[t])
+        assert torch.equal(o1.slots[0], out.slots[t])
+        close(o1.weights[0].cpu().numpy(), out.weights[t].cpu().numpy(), "weights")
+        close(y1.cpu().numpy(), y[t].cpu().numpy(), f"y token {t}")
+
+
+def test_prefill_early_out(real):
+    w = real.w
+    x = synth.activations(w, 16, stream=6)
+    r = oracle_route(real, 0, x)
+    table = real.table.copy()
+    table[0, r.ids[7][9]] = -1
+    hole = DeviceModel(w, table=table, pool=real.pool)
+    out, y, _ = run_chunk(hole, x, 512)
+    assert int(out.early_out.cpu()[0]) == 1
+    assert int(out.miss_count.cpu()[0]) == int((r.ids == r.ids[7][9]).sum())
+    assert torch.isnan(y).all()
+
+
+@pytest.mark.parametrize("H,E,k,F,qbits,T,cap", [
+    (256, 16, 2, 64, 3, 9, 16), (512, 100, 5, 128, 2, 33, 20), (1024, 1024, 32, 256, 2, 17, 1024),
+    (256, 8, 1, 32, 3, 70, 3), (2048, 64, 8, 2048, 2, 12, 64), (512, 200, 7, 1024, 3, 21, 30)])
+def test_prefill_shapes(H, E, k, F, qbits, T, cap):
+    rng = np.random.default_rng(H + E + k + F + qbits + T)
+    n = H * F
+    W = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32)
+    table = rng.permutation(E).astype(np.int32)[None, :]
+    pool_np = np.stack([np.concatenate([synth.random_tensor(rng, n, qbits) for _ in range(3)])
+                        for _ in range(E)])
+    d = B.desc(H, E, k, F, 1, qbits, E)
+    pool = to_dev(pool_np)
+    scratch = torch.zeros(B.rl_prefill_scratch_bytes(d, T), dtype=torch.uint8, device="cuda")
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    out = RouteBuffers.alloc(T, k, E)
+    y = torch.full((T, H), float("nan"), device="cuda")
+    B.moe_prefill_chunk(d, 0, T, cap, to_dev(x), to_dev(W), to_dev(bias), to_dev(table), pool,
+                        out.c(), scratch, scratch.numel(), y)
+    r, plan, y_ref = O.prefill_chunk(O.LayerShape(H, E, k, F, qbits), x, W, bias, table[0],
+                                     lambda s: pool_np[s], cap)
+    check_route(out, r)
+    close(y.cpu().numpy(), y_ref, "y")
