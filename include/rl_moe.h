@@ -176,8 +176,8 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
                       void* scratch, int64_t scratch_bytes, float* y,
                       void* stream);
 
-/* Stage entry points, for tests and benchmarks: each enqueues exactly one
- * kernel of a path above, with the same arguments and scratch layout.
+/* Stage entry points, for tests and benchmarks: each enqueues the kernels of
+ * one step of a path above, with the same arguments and scratch layout.
  *   rl_decode_stage: stage 1 = gate/up GEMVs + SwiGLU of the k selected
  *     experts (needs `route` filled by rl_route for this token; h goes to
  *     scratch); stage 2 = down GEMVs + rank-ordered sum into y (needs stage 1

@@ -50,7 +50,8 @@ DecodeLayout decode_layout(const rl_moe_desc* d, int T) {
 // pair intermediates.
 struct PrefillLayout {
   rl_prefill_layout pub;
-  int64_t logits, counts, offs, bucket_slot, tile_start, n_tiles, hbuf, ebuf, total;
+  int64_t logits, counts, offs, bucket_slot, tile_start, n_tiles, hbuf, ebuf, xq, xe, hq, he,
+      total;
 };
 PrefillLayout prefill_layout(const rl_moe_desc* d, int T) {
   PrefillLayout l;
@@ -76,6 +77,10 @@ PrefillLayout prefill_layout(const rl_moe_desc* d, int T) {
   l.n_tiles = take(4);
   l.hbuf = take(P * d->width * 4);
   l.ebuf = take(P * d->hidden * 4);
+  l.xq = take(int64_t(T) * d->hidden * 4);
+  l.xe = take(int64_t(T) * (d->hidden / 256) * 4);
+  l.hq = take(P * d->width * 4);
+  l.he = take(P * ((d->width + 255) / 256) * 4);
   l.total = off;
   l.pub.total = off;
   return l;
@@ -178,6 +183,12 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
   a.plan.n_tiles = i32(l.n_tiles);
   a.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   a.ebuf = reinterpret_cast<float*>(s + l.ebuf);
+  a.xq = s + l.xq;
+  a.xe = i32(l.xe);
+  a.hq = s + l.hq;
+  a.he = i32(l.he);
+  a.mfma = d->qbits == 2 && d->width % 256 == 0;
+  a.tile_tokens = a.mfma ? 12 : 8;
   a.y = y;
   return a;
 }

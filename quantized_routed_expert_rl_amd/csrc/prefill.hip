@@ -10,7 +10,7 @@
 
 namespace rl {
 
-constexpr int kTileTokens = 8;   // tokens of one bucket handled together
+constexpr int kTileTokens = 8;   // tokens of one bucket per VALU work item
 
 // ----------------------------------------------------------------- plan
 // Greedy consecutive token groups, one wave.  A token joins the current
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     const uint32_t* __restrict__ early_out, const int32_t* __restrict__ n_groups,
     const int32_t* __restrict__ counts, int32_t* offs, int32_t* n_buckets,
     int32_t* group_bucket_start, int32_t* bucket_expert, int32_t* bucket_start,
-    int32_t* bucket_slot, int32_t* tile_start, int32_t* n_tiles) {
+    int32_t* bucket_slot, int32_t* tile_start, int32_t* n_tiles, int tile_tokens) {
   if (*early_out) return;
   const int ng = *n_groups;
   const int n = ng * E;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   for (int base = 0; base < n; base += 1024) {
     const int i = base + threadIdx.x;
     const int c = i < n ? counts[i] : 0;
-    int v[3] = {c, c > 0 ? 1 : 0, (c + kTileTokens - 1) / kTileTokens};
+    int v[3] = {c, c > 0 ? 1 : 0, (c + tile_tokens - 1) / tile_tokens};
     int tot[3];
     block_scan3(v, tot);
     if (i < n) {
@@ -344,7 +344,7 @@ void launch_prefill_plan(const PrefillArgs& a, hipStream_t st) {
   plan_scan_kernel<<<1, 1024, 0, st>>>(a.E, a.layer, a.residency, a.early_out, p.n_groups,
                                        p.counts, p.offs, p.n_buckets, p.group_bucket_start,
                                        p.bucket_expert, p.bucket_start, p.bucket_slot,
-                                       p.tile_start, p.n_tiles);
+                                       p.tile_start, p.n_tiles, a.tile_tokens);
   plan_pairs_kernel<true><<<blocks, 256, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
                                                   p.group_bounds, nullptr, p.offs, p.pairs);
 }
@@ -391,11 +391,25 @@ static void down_q(const PrefillArgs& a, hipStream_t st) {
 }
 
 void launch_prefill_gateup(const PrefillArgs& a, hipStream_t st) {
-  if (a.qbits == 3) gateup_q<3>(a, st); else gateup_q<2>(a, st);
+  if (a.mfma) {
+    launch_quantize_x(a, st);
+    launch_prefill_gateup_mfma(a, st);
+  } else if (a.qbits == 3) {
+    gateup_q<3>(a, st);
+  } else {
+    gateup_q<2>(a, st);
+  }
 }
 
 void launch_prefill_down(const PrefillArgs& a, hipStream_t st) {
-  if (a.qbits == 3) down_q<3>(a, st); else down_q<2>(a, st);
+  if (a.mfma) {
+    launch_quantize_h(a, st);
+    launch_prefill_down_mfma(a, st);
+  } else if (a.qbits == 3) {
+    down_q<3>(a, st);
+  } else {
+    down_q<2>(a, st);
+  }
 }
 
 void launch_prefill_sum(const PrefillArgs& a, hipStream_t st) {

@@ -65,14 +65,24 @@ struct PrefillArgs {
   const float* weights;
   const uint32_t* early_out;
   PlanPtrs plan;
-  float* hbuf;   // [T*k][F], rows in sorted pair order
-  float* ebuf;   // [T*k][H], rows by pair id p = t*k + r
+  bool mfma;        // int8 matrix-core path (2-bit, F % 256 == 0)
+  int tile_tokens;  // tokens per token tile of a bucket
+  float* hbuf;      // [T*k][F], rows in sorted pair order
+  float* ebuf;      // [T*k][H], rows by pair id p = t*k + r
+  uint8_t* xq;      // [T][H*4] digit operands of x (MFMA path)
+  int32_t* xe;      // [T][H/256] exponents of x
+  uint8_t* hq;      // [T*k][F*4] digit operands of h (MFMA path)
+  int32_t* he;      // [T*k][F/256] exponents of h
   float* y;
 };
 void launch_prefill_plan(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_gateup(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_down(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_sum(const PrefillArgs& a, hipStream_t st);
+void launch_quantize_x(const PrefillArgs& a, hipStream_t st);
+void launch_quantize_h(const PrefillArgs& a, hipStream_t st);
+void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st);
+void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st);
 
 void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st);
 void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,
