@@ -11,7 +11,7 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librlmoe.so")
+LIB_PATH = os.environ.get("RLMOE_LIB") or os.path.join(_HERE, "librlmoe.so")
 
 RL_OK, RL_E_INVAL, RL_E_SHAPE, RL_E_RANGE, RL_E_SCRATCH, RL_E_DEVICE = 0, -1, -2, -3, -4, -5
 

@@ -50,7 +50,7 @@ DecodeLayout decode_layout(const rl_moe_desc* d, int T) {
 // pair intermediates.
 struct PrefillLayout {
   rl_prefill_layout pub;
-  int64_t logits, counts, offs, bucket_slot, tile_start, n_tiles, hbuf, ebuf, xq, xe, hq, he,
+  int64_t logits, counts, offs, bucket_slot, tile_start, tile_bucket, n_tiles, hbuf, ebuf, xq, xe, hq, he,
       total;
 };
 PrefillLayout prefill_layout(const rl_moe_desc* d, int T) {
@@ -74,6 +74,7 @@ PrefillLayout prefill_layout(const rl_moe_desc* d, int T) {
   l.offs = take(int64_t(T) * E * 4);
   l.bucket_slot = take(P * 4);
   l.tile_start = take((P + 1) * 4);
+  l.tile_bucket = take(P * 4);
   l.n_tiles = take(4);
   l.hbuf = take(P * d->width * 4);
   l.ebuf = take(P * d->hidden * 4);
@@ -180,6 +181,7 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
   a.plan.offs = i32(l.offs);
   a.plan.bucket_slot = i32(l.bucket_slot);
   a.plan.tile_start = i32(l.tile_start);
+  a.plan.tile_bucket = i32(l.tile_bucket);
   a.plan.n_tiles = i32(l.n_tiles);
   a.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   a.ebuf = reinterpret_cast<float*>(s + l.ebuf);

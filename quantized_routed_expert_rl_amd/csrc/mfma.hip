@@ -126,18 +126,24 @@ __device__ inline v4i dequant_dword(uint32_t w, uint32_t lut) {
 }
 
 // One lane's share of a 16-row x 256-column block tile of a tensor.
+// Raw bytes only: nothing is computed from a load when it is issued, so a
+// prefetched tile does not make the wave wait.
 struct TileCodes {
   uint4 c;       // 64 codes: K = 64q .. 64q+63 of the block, row l%16
   uint32_t s;    // group scales of groups 2q (low nibble) and 2q+1
-  float dq;      // d / 32 of the lane's row
+  uint32_t dh;   // block scale d of the lane's row, binary16 bits
 };
 
 __device__ inline TileCodes load_tile(const uint8_t* t, const PoolView& p, int64_t blk, int q) {
   TileCodes r;
   r.c = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 16 * q);
   r.s = t[p.s + 4 * blk + q];
-  r.dq = half_bits_to_float(*reinterpret_cast<const uint16_t*>(t + p.d + 2 * blk)) * (1.f / 32.f);
+  r.dh = *reinterpret_cast<const uint16_t*>(t + p.d + 2 * blk);
   return r;
+}
+
+__device__ inline float tile_dq(const TileCodes& t) {
+  return half_bits_to_float(uint16_t(t.dh)) * (1.f / 32.f);
 }
 
 __device__ inline void dequant_tile(const TileCodes& tc, v4i A[4]) {
@@ -148,13 +154,6 @@ __device__ inline void dequant_tile(const TileCodes& tc, v4i A[4]) {
   A[3] = dequant_dword(tc.c.w, l1);
 }
 
-// d/32 of the output rows 4*(l/16)+v, fetched from the lanes that own them.
-__device__ inline void out_row_scales(float dq, float dsc[4]) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) dsc[v] = __shfl(dq, 4 * (l >> 4) + v, kWave);
-}
-
 __device__ inline v4i mfma4(const v4i A[4], const v4i B[4]) {
   v4i D = {0, 0, 0, 0};
 #pragma unroll
@@ -162,224 +161,187 @@ __device__ inline v4i mfma4(const v4i A[4], const v4i B[4]) {
   return D;
 }
 
-__device__ inline void load_b(const uint8_t* rowq, int kb, int q, int dj, v4i B[4]) {
-  const int4* p = reinterpret_cast<const int4*>(rowq + ((kb * 4 + q) * 4 + dj) * 64);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int4 v = p[m];
-    B[m] = v4i{v.x, v.y, v.z, v.w};
-  }
-}
+// -------------------------------------------------- batched projections
+// One kernel for both projections.  Work item = (token tile of <= 12 tokens
+// of one bucket, 128 rows j of gate and up) or (token tile, 256 rows i of
+// down).  Block = 8 waves over the same token tile; wave w owns two 16-row
+// tiles: gate and up of rows j0+16w (gate/up), or rows i0+32w and i0+32w+16
+// (down).  K runs over 256-value blocks: the tile's digit operands for block
+// kb+1 are copied to LDS (double buffer) and the wave's codes for kb+1 are
+// loaded while block kb computes.  The three 4-token column tiles give three
+// independent MFMA chains per row tile, issued interleaved.
+constexpr int kProjWaves = 8;
 
-__device__ inline int tile_bucket_m(const int32_t* tile_start, int nb, int tile) {
-  int lo = 0, hi = nb - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// ------------------------------------------------------------ gate / up
-// Work item = (token tile of <= 12 tokens of one bucket, 64 rows j).  One
-// wave per item: four 16-row tiles of gate and of up over all H/256 blocks;
-// then h = silu(g) * u for the item's rows and tokens.
-__global__ __launch_bounds__(64) void prefill_gateup_mfma_kernel(
-    PoolView pv, int H, int F, int k, const uint8_t* __restrict__ xq,
-    const int32_t* __restrict__ xe, const uint32_t* __restrict__ early_out,
-    const int32_t* __restrict__ n_buckets_p, const int32_t* __restrict__ n_tiles_p,
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
+    PoolView pv, int H, int F, int k, const uint8_t* __restrict__ aq,
+    const int32_t* __restrict__ ae, const uint32_t* __restrict__ early_out,
+    const int32_t* __restrict__ n_tiles_p, const int32_t* __restrict__ tile_bucket,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ bucket_start,
     const int32_t* __restrict__ bucket_slot, const int32_t* __restrict__ pairs,
-    float* __restrict__ hbuf) {
+    float* __restrict__ out) {
   if (*early_out) return;
-  const int l = threadIdx.x;
+  __shared__ __align__(16) uint8_t s_b[2][kMT * 1024];
+  __shared__ int s_row[kMT];            // operand row of each token slot
+  __shared__ __align__(16) float s_rs[kProjWaves][2][16];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int row = l & 15, q = l >> 4, tk = (l & 15) >> 2, dj = l & 3;
-  const int nb = *n_buckets_p, ntiles = *n_tiles_p;
-  const int njr = F / 64, HB = H / 256;
-  for (int item = blockIdx.x; item < ntiles * njr; item += gridDim.x) {
-    const int tile = item / njr, jr = item % njr;
-    const int b = tile_bucket_m(tile_start, nb, tile);
+  const int K = GATEUP ? H : F;          // reduction length
+  const int NR = GATEUP ? F : H;         // output rows
+  const int KB = K / 256;
+  const int rows_per_item = GATEUP ? 128 : 256;
+  const int nri = NR / rows_per_item;
+  const int ntiles = *n_tiles_p;
+  for (int item = blockIdx.x; item < ntiles * nri; item += gridDim.x) {
+    const int tile = item / nri, ri = item % nri;
+    const int b = tile_bucket[tile];
     const int pos0 = bucket_start[b] + (tile - tile_start[b]) * kMT;
     const int rem = bucket_start[b + 1] - pos0;
     const int nt = rem < kMT ? rem : kMT;
-    const int nct = (nt + 3) >> 2;
     const int slot = bucket_slot[b];
-    const uint8_t* tens[2] = {tensor_base(pv, slot, 0), tensor_base(pv, slot, 1)};
-    const uint8_t* xrow[3];
-    float fct[3];
+    __syncthreads();                     // previous item done with s_b, s_row
+    if (tid < nt) s_row[tid] = GATEUP ? pairs[pos0 + tid] / k : pos0 + tid;
+    __syncthreads();
+    const uint8_t* t0p = tensor_base(pv, slot, GATEUP ? 0 : 2);
+    const uint8_t* t1p = tensor_base(pv, slot, GATEUP ? 1 : 2);
+    const int r00 = GATEUP ? ri * 128 + 16 * w : ri * 256 + 32 * w;
+    const int r01 = GATEUP ? r00 : r00 + 16;
+    const int64_t blk0 = int64_t(r00 + row) * KB, blk1 = int64_t(r01 + row) * KB;
     bool tok_ok[3];
+    int orow[3];
 #pragma unroll
     for (int ct = 0; ct < 3; ++ct) {
-      const int n = 4 * ct + tk;
-      tok_ok[ct] = n < nt;
-      const int t = tok_ok[ct] ? pairs[pos0 + n] / k : 0;
-      xrow[ct] = xq + int64_t(t) * H * 4;
-      fct[ct] = ldexpf(1.f, 8 * (3 - dj) - (tok_ok[ct] ? xe[int64_t(t) * HB] : 0));
+      tok_ok[ct] = 4 * ct + tk < nt;
+      orow[ct] = s_row[tok_ok[ct] ? 4 * ct + tk : 0];
     }
-    float acc[2][4][3][4];
+    // operand copy: 12 slots x 1 KB = 768 chunks of 16 B; thread takes chunk
+    // tid and tid+512 (the second only for tid < 256); empty slots get zeros
+    const int c0 = tid, c1 = tid + 512;
+    const uint32_t m0 = c0 < nt * 64 ? ~0u : 0u;
+    const uint32_t m1 = (c1 < 768 && c1 < nt * 64) ? ~0u : 0u;
+    const uint8_t* src0 = aq + int64_t(s_row[m0 ? (c0 >> 6) : 0]) * K * 4 + (c0 & 63) * 16;
+    const uint8_t* src1 = aq + int64_t(s_row[m1 ? (c1 >> 6) : 0]) * K * 4 + (c1 & 63) * 16;
+    float acc[2][3][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[a][rt][ct][v] = 0.f;
-    for (int kb = 0; kb < HB; ++kb) {
-      TileCodes tc[2][4];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          tc[a][rt] = load_tile(tens[a], pv, int64_t(jr * 64 + rt * 16 + row) * HB + kb, q);
-      v4i B[3][4];
-#pragma unroll
-      for (int ct = 0; ct < 3; ++ct) {
-        if (ct < nct && tok_ok[ct]) {
-          load_b(xrow[ct], kb, q, dj, B[ct]);
-        } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) B[ct][m] = v4i{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          v4i A[4];
-          dequant_tile(tc[a][rt], A);
-          float dsc[4];
-          out_row_scales(tc[a][rt].dq, dsc);
-#pragma unroll
-          for (int ct = 0; ct < 3; ++ct) {
-            if (ct < nct) {
-              const v4i D = mfma4(A, B[ct]);
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                acc[a][rt][ct][v] = fmaf(dsc[v], float(D[v]), acc[a][rt][ct][v]);
-            }
-          }
-        }
-      }
-    }
-    // combine the 4 digit columns of each token and apply SwiGLU
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int ct = 0; ct < 3; ++ct) {
-        if (ct < nct) {
-          float h[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float g = acc[0][rt][ct][v] * fct[ct];
-            float u = acc[1][rt][ct][v] * fct[ct];
-            g += __shfl_xor(g, 1, kWave);
-            g += __shfl_xor(g, 2, kWave);
-            u += __shfl_xor(u, 1, kWave);
-            u += __shfl_xor(u, 2, kWave);
-            h[v] = silu_mul(g, u);
-          }
-          if (dj == 0 && tok_ok[ct]) {
-            const int n = 4 * ct + tk;
-            *reinterpret_cast<float4*>(hbuf + int64_t(pos0 + n) * F + jr * 64 + rt * 16 + 4 * q) =
-                make_float4(h[0], h[1], h[2], h[3]);
-          }
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ down
-// Work item = (token tile, 64 rows i).  B = the tile's h rows as digits with
-// one exponent per (pair, 256-value block).  Output rows go to ebuf row p.
-__global__ __launch_bounds__(64) void prefill_down_mfma_kernel(
-    PoolView pv, int H, int F, const uint8_t* __restrict__ hq, const int32_t* __restrict__ he,
-    const uint32_t* __restrict__ early_out, const int32_t* __restrict__ n_buckets_p,
-    const int32_t* __restrict__ n_tiles_p, const int32_t* __restrict__ tile_start,
-    const int32_t* __restrict__ bucket_start, const int32_t* __restrict__ bucket_slot,
-    const int32_t* __restrict__ pairs, float* __restrict__ ebuf) {
-  if (*early_out) return;
-  const int l = threadIdx.x;
-  const int row = l & 15, q = l >> 4, tk = (l & 15) >> 2, dj = l & 3;
-  const int nb = *n_buckets_p, ntiles = *n_tiles_p;
-  const int nir = H / 64, FB = F / 256;
-  for (int item = blockIdx.x; item < ntiles * nir; item += gridDim.x) {
-    const int tile = item / nir, ir = item % nir;
-    const int b = tile_bucket_m(tile_start, nb, tile);
-    const int pos0 = bucket_start[b] + (tile - tile_start[b]) * kMT;
-    const int rem = bucket_start[b + 1] - pos0;
-    const int nt = rem < kMT ? rem : kMT;
-    const int nct = (nt + 3) >> 2;
-    const uint8_t* down = tensor_base(pv, bucket_slot[b], 2);
-    bool tok_ok[3];
-    int pos[3];
-#pragma unroll
-    for (int ct = 0; ct < 3; ++ct) {
-      const int n = 4 * ct + tk;
-      tok_ok[ct] = n < nt;
-      pos[ct] = tok_ok[ct] ? pos0 + n : pos0;
-    }
-    float acc[4][3][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int ct = 0; ct < 3; ++ct)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[rt][ct][v] = 0.f;
-    for (int kb = 0; kb < FB; ++kb) {
-      TileCodes tc[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        tc[rt] = load_tile(down, pv, int64_t(ir * 64 + rt * 16 + row) * FB + kb, q);
-      v4i B[3][4];
-      float fct[3];
+        for (int v = 0; v < 4; ++v) acc[u][ct][v] = 0.f;
+    uint4 cr0, cr1;
+    TileCodes ta0, ta1, tb0, tb1;        // double-buffered codes of the two tiles
+    cr0 = *reinterpret_cast<const uint4*>(src0);
+    cr1 = *reinterpret_cast<const uint4*>(src1);
+    ta0 = load_tile(t0p, pv, blk0, q);
+    ta1 = load_tile(t1p, pv, blk1, q);
+    *reinterpret_cast<uint4*>(&s_b[0][c0 * 16]) =
+        make_uint4(cr0.x & m0, cr0.y & m0, cr0.z & m0, cr0.w & m0);
+    if (c1 < 768)
+      *reinterpret_cast<uint4*>(&s_b[0][c1 * 16]) =
+          make_uint4(cr1.x & m1, cr1.y & m1, cr1.z & m1, cr1.w & m1);
+    __syncthreads();
+    for (int kb = 0; kb < KB; ++kb) {
+      const int buf = kb & 1;
+      const bool more = kb + 1 < KB;
+      if (more) {
+        cr0 = *reinterpret_cast<const uint4*>(src0 + (kb + 1) * 1024);
+        cr1 = *reinterpret_cast<const uint4*>(src1 + (kb + 1) * 1024);
+        tb0 = load_tile(t0p, pv, blk0 + kb + 1, q);
+        tb1 = load_tile(t1p, pv, blk1 + kb + 1, q);
+      }
+      // d/32 of output rows 4q+v of both tiles, through LDS
+      if (q == 0) {
+        s_rs[w][0][row] = tile_dq(ta0);
+        s_rs[w][1][row] = tile_dq(ta1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const float4 ds0 = *reinterpret_cast<const float4*>(&s_rs[w][0][4 * q]);
+      const float4 ds1 = *reinterpret_cast<const float4*>(&s_rs[w][1][4 * q]);
+      v4i A0[4], A1[4];
+      dequant_tile(ta0, A0);
+      dequant_tile(ta1, A1);
+      v4i D0[3], D1[3];
 #pragma unroll
       for (int ct = 0; ct < 3; ++ct) {
-        if (ct < nct && tok_ok[ct]) {
-          load_b(hq + int64_t(pos[ct]) * F * 4, kb, q, dj, B[ct]);
-          fct[ct] = ldexpf(1.f, 8 * (3 - dj) - he[int64_t(pos[ct]) * FB + kb]);
-        } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) B[ct][m] = v4i{0, 0, 0, 0};
-          fct[ct] = 0.f;
-        }
+        D0[ct] = v4i{0, 0, 0, 0};
+        D1[ct] = v4i{0, 0, 0, 0};
       }
+      const uint8_t* bb = &s_b[buf][tk * 1024 + q * 256 + dj * 64];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        v4i A[4];
-        dequant_tile(tc[rt], A);
-        float dsc[4];
-        out_row_scales(tc[rt].dq, dsc);
+      for (int m = 0; m < 4; ++m) {
+        v4i Bm[3];
 #pragma unroll
         for (int ct = 0; ct < 3; ++ct) {
-          if (ct < nct) {
-            const v4i D = mfma4(A, B[ct]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[rt][ct][v] = fmaf(dsc[v] * fct[ct], float(D[v]), acc[rt][ct][v]);
-          }
+          const int4 v = *reinterpret_cast<const int4*>(bb + ct * 4096 + m * 16);
+          Bm[ct] = v4i{v.x, v.y, v.z, v.w};
         }
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct)
+          D0[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[m], Bm[ct], D0[ct], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct)
+          D1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[m], Bm[ct], D1[ct], 0, 0, 0);
       }
+      float f[3] = {1.f, 1.f, 1.f};
+      if (!GATEUP) {
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct) f[ct] = ldexpf(1.f, 8 * (3 - dj) - ae[int64_t(orow[ct]) * KB + kb]);
+      }
+      const float s0[4] = {ds0.x, ds0.y, ds0.z, ds0.w}, s1[4] = {ds1.x, ds1.y, ds1.z, ds1.w};
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[0][ct][v] = fmaf(s0[v] * f[ct], float(D0[ct][v]), acc[0][ct][v]);
+          acc[1][ct][v] = fmaf(s1[v] * f[ct], float(D1[ct][v]), acc[1][ct][v]);
+        }
+      if (more) {
+        *reinterpret_cast<uint4*>(&s_b[buf ^ 1][c0 * 16]) =
+            make_uint4(cr0.x & m0, cr0.y & m0, cr0.z & m0, cr0.w & m0);
+        if (c1 < 768)
+          *reinterpret_cast<uint4*>(&s_b[buf ^ 1][c1 * 16]) =
+              make_uint4(cr1.x & m1, cr1.y & m1, cr1.z & m1, cr1.w & m1);
+        ta0 = tb0;
+        ta1 = tb1;
+      }
+      __syncthreads();
     }
+    // combine each token's 4 digit columns; store
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int ct = 0; ct < 3; ++ct) {
+      const int n = 4 * ct + tk;
+      if (GATEUP) {
+        const float fx = ldexpf(1.f, 8 * (3 - dj) - (tok_ok[ct] ? ae[int64_t(orow[ct]) * KB] : 0));
+        float h[4];
 #pragma unroll
-      for (int ct = 0; ct < 3; ++ct) {
-        if (ct < nct) {
+        for (int v = 0; v < 4; ++v) {
+          float g = acc[0][ct][v] * fx, u = acc[1][ct][v] * fx;
+          g += __shfl_xor(g, 1, kWave);
+          g += __shfl_xor(g, 2, kWave);
+          u += __shfl_xor(u, 1, kWave);
+          u += __shfl_xor(u, 2, kWave);
+          h[v] = silu_mul(g, u);
+        }
+        if (dj == 0 && tok_ok[ct])
+          *reinterpret_cast<float4*>(out + int64_t(pos0 + n) * F + r00 + 4 * q) =
+              make_float4(h[0], h[1], h[2], h[3]);
+      } else {
+        const int p = tok_ok[ct] ? pairs[pos0 + n] : 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
           float e[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            float s = acc[rt][ct][v];
-            s += __shfl_xor(s, 1, kWave);
-            s += __shfl_xor(s, 2, kWave);
-            e[v] = s;
+            float sv = acc[u][ct][v];
+            sv += __shfl_xor(sv, 1, kWave);
+            sv += __shfl_xor(sv, 2, kWave);
+            e[v] = sv;
           }
-          if (dj == 0 && tok_ok[ct]) {
-            const int p = pairs[pos[ct]];
-            *reinterpret_cast<float4*>(ebuf + int64_t(p) * H + ir * 64 + rt * 16 + 4 * q) =
+          if (dj == 0 && tok_ok[ct])
+            *reinterpret_cast<float4*>(out + int64_t(p) * H + (u ? r01 : r00) + 4 * q) =
                 make_float4(e[0], e[1], e[2], e[3]);
-          }
         }
       }
     }
@@ -393,13 +355,6 @@ void launch_quantize_x(const PrefillArgs& a, hipStream_t st) {
                                                                      a.early_out);
 }
 
-void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
-  const PlanPtrs& p = a.plan;
-  prefill_gateup_mfma_kernel<<<2048, 64, 0, st>>>(
-      a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_buckets, p.n_tiles, p.tile_start,
-      p.bucket_start, p.bucket_slot, p.pairs, a.hbuf);
-}
-
 void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
   const int rpb = 256 / (a.F / 16);
   const int R = a.T * a.k;
@@ -407,10 +362,17 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
                                                                     a.early_out);
 }
 
+void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
+  const PlanPtrs& p = a.plan;
+  prefill_proj_mfma_kernel<true><<<512, 512, 0, st>>>(
+      a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
+      p.bucket_start, p.bucket_slot, p.pairs, a.hbuf);
+}
+
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  prefill_down_mfma_kernel<<<2048, 64, 0, st>>>(
-      a.pool, a.H, a.F, a.hq, a.he, a.early_out, p.n_buckets, p.n_tiles, p.tile_start,
+  prefill_proj_mfma_kernel<false><<<512, 512, 0, st>>>(
+      a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
       p.bucket_start, p.bucket_slot, p.pairs, a.ebuf);
 }
 

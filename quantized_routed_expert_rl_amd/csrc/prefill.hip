@@ -123,6 +123,8 @@ __device__ inline void block_scan3(int v[3], int tot[3]) {
   __syncthreads();
 }
 
+__device__ inline int v2_tiles(int c, int tile_tokens) { return (c + tile_tokens - 1) / tile_tokens; }
+
 // Offsets of every (group, expert) run of pairs, the bucket list, each
 // bucket's slot and its first token tile.
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
@@ -130,7 +132,8 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
     const uint32_t* __restrict__ early_out, const int32_t* __restrict__ n_groups,
     const int32_t* __restrict__ counts, int32_t* offs, int32_t* n_buckets,
     int32_t* group_bucket_start, int32_t* bucket_expert, int32_t* bucket_start,
-    int32_t* bucket_slot, int32_t* tile_start, int32_t* n_tiles, int tile_tokens) {
+    int32_t* bucket_slot, int32_t* tile_start, int32_t* n_tiles, int32_t* tile_bucket,
+    int tile_tokens) {
   if (*early_out) return;
   const int ng = *n_groups;
   const int n = ng * E;
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
         bucket_start[b] = carry[0] + v[0];
         bucket_slot[b] = residency[int64_t(layer) * E + e];
         tile_start[b] = carry[2] + v[2];
+        for (int u = 0; u < v2_tiles(c, tile_tokens); ++u) tile_bucket[carry[2] + v[2] + u] = b;
       }
     }
 #pragma unroll
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
 
 // ---------------------------------------------------- batched experts
 // Bucket of a token tile: last b with tile_start[b] <= tile.
-__device__ inline int tile_bucket(const int32_t* tile_start, int nb, int tile) {
+__device__ inline int find_tile_bucket(const int32_t* tile_start, int nb, int tile) {
   int lo = 0, hi = nb - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(
   const int seg = lane % LPR, rs = lane / LPR;
   const int nb = *n_buckets_p, ntiles = *n_tiles_p;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int b = tile_bucket(tile_start, nb, tile);
+    const int b = find_tile_bucket(tile_start, nb, tile);
     const int pos0 = bucket_start[b] + (tile - tile_start[b]) * kTileTokens;
     const int pend = bucket_start[b + 1];
     const int nt = pend - pos0 < kTileTokens ? pend - pos0 : kTileTokens;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(
   const int nrt = (H + ROWS - 1) / ROWS;
   for (int item = blockIdx.x; item < ntiles * nrt; item += gridDim.x) {
     const int tile = item / nrt, rt = item % nrt;
-    const int b = tile_bucket(tile_start, nb, tile);
+    const int b = find_tile_bucket(tile_start, nb, tile);
     const int pos0 = bucket_start[b] + (tile - tile_start[b]) * kTileTokens;
     const int pend = bucket_start[b + 1];
     const int nt = pend - pos0 < kTileTokens ? pend - pos0 : kTileTokens;
@@ -344,7 +348,7 @@ void launch_prefill_plan(const PrefillArgs& a, hipStream_t st) {
   plan_scan_kernel<<<1, 1024, 0, st>>>(a.E, a.layer, a.residency, a.early_out, p.n_groups,
                                        p.counts, p.offs, p.n_buckets, p.group_bucket_start,
                                        p.bucket_expert, p.bucket_start, p.bucket_slot,
-                                       p.tile_start, p.n_tiles, a.tile_tokens);
+                                       p.tile_start, p.n_tiles, p.tile_bucket, a.tile_tokens);
   plan_pairs_kernel<true><<<blocks, 256, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
                                                   p.group_bounds, nullptr, p.offs, p.pairs);
 }

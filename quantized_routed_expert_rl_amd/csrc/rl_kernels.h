@@ -52,6 +52,7 @@ struct PlanPtrs {
   int32_t* offs;          // [max_groups*E]
   int32_t* bucket_slot;   // [T*k]
   int32_t* tile_start;    // [T*k+1] token tiles before each bucket
+  int32_t* tile_bucket;   // [T*k] bucket of each token tile
   int32_t* n_tiles;       // [1]
 };
 

@@ -166,58 +166,66 @@ __global__ __launch_bounds__(64) void route_gemv_topk_kernel(
 }
 
 // ------------------------------------------------------- T > 1: GEMM
-// logits[t][e] = fl32(sum_i W[e][i] x[t][i] + b[e]) with float64 FMAs.
-// 32x32 output tile per block of 256 threads, 2x2 outputs per thread,
-// K staged through LDS in float64 in chunks of 32.
+// logits[t][e] = fl32(sum_i W[e][i] x[t][i] + b[e]) on the float64 matrix
+// cores (v_mfma_f64_16x16x4f64; A lane l: row l%16, K index l/16; B lane l:
+// column l%16, K index l/16; output lane l, v: row l/16 + 4v, column l%16).
+// Block = 32 tokens x 32 experts, one 16x16 tile per wave over all of K.
+// Inside each 16-value chunk c, MFMA step 4c+i of lane quad kq takes K index
+// 16c + 4kq + i for both operands, so each lane reads float4s.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void route_gemm_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
     int T, int E, int H, float* __restrict__ logits, float* __restrict__ logits_out,
     uint32_t* miss_count, uint32_t* early_out) {
-  constexpr int TB = 32, KC = 32;
-  __shared__ double Xs[TB][KC + 1];
-  __shared__ double Ws[TB][KC + 1];
-  const int t0 = blockIdx.y * TB, e0 = blockIdx.x * TB;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.y * 32 + (wv >> 1) * 16, e0 = blockIdx.x * 32 + (wv & 1) * 16;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     *miss_count = 0u;
     *early_out = 0u;
   }
-  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-  for (int k0 = 0; k0 < H; k0 += KC) {
-    // 32 rows x 32 cols of each operand: 1024 values, 4 per thread
+  const int r = l & 15, kq = l >> 4;
+  const int ta = t0 + r, eb = e0 + r;
+  const bool va = ta < T, vb = eb < E;
+  const float* xa = x + int64_t(va ? ta : 0) * H + 4 * kq;
+  const float* wb = W + int64_t(vb ? eb : 0) * H + 4 * kq;
+  // four independent accumulation chains (one per 16-value chunk of each
+  // 64-value step) keep the matrix core busy; summed in float64 at the end
+  v4d acc4[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int li = tid + 256 * q;
-      const int rr = li >> 5, cc = li & 31;
-      const int t = t0 + rr, e = e0 + rr;
-      Xs[rr][cc] = t < T ? double(x[int64_t(t) * H + k0 + cc]) : 0.0;
-      Ws[rr][cc] = e < E ? double(W[int64_t(e) * H + k0 + cc]) : 0.0;
+  for (int u = 0; u < 4; ++u) acc4[u] = v4d{0.0, 0.0, 0.0, 0.0};
+  for (int c = 0; c < H; c += 64) {
+    float4 av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = va ? *reinterpret_cast<const float4*>(xa + c + 16 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+      bv[u] = vb ? *reinterpret_cast<const float4*>(wb + c + 16 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < KC; ++kk) {
-      const double a0 = Xs[2 * ty][kk], a1 = Xs[2 * ty + 1][kk];
-      const double b0 = Ws[2 * tx][kk], b1 = Ws[2 * tx + 1][kk];
-      acc[0][0] = fma(a0, b0, acc[0][0]);
-      acc[0][1] = fma(a0, b1, acc[0][1]);
-      acc[1][0] = fma(a1, b0, acc[1][0]);
-      acc[1][1] = fma(a1, b1, acc[1][1]);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].x), double(bv[u].x), acc4[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].y), double(bv[u].y), acc4[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].z), double(bv[u].z), acc4[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].w), double(bv[u].w), acc4[u], 0, 0, 0);
   }
+  const v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = t0 + 2 * ty + i, e = e0 + 2 * tx + j;
-      if (t < T && e < E) {
-        double v = acc[i][j];
-        if (bias) v += double(bias[e]);
-        const float l = float(v);
-        logits[int64_t(t) * E + e] = l;
-        if (logits_out) logits_out[int64_t(t) * E + e] = l;
-      }
+  for (int v = 0; v < 4; ++v) {
+    const int t = t0 + kq + 4 * v, e = e0 + r;
+    if (t < T && e < E) {
+      double s = acc[v];
+      if (bias) s += double(bias[e]);
+      const float lg = float(s);
+      logits[int64_t(t) * E + e] = lg;
+      if (logits_out) logits_out[int64_t(t) * E + e] = lg;
     }
+  }
 }
 
 // One wave per token: selection, weights, lookup; misses summed atomically.
