@@ -121,12 +121,25 @@ def main():
     with torch.cuda.stream(stream):
         eager_ms = event_ms(decode_step, stream, 3)
 
-    # dominant kernel: gate/up GEMVs + SwiGLU of the 10 selected experts, one
-    # launch per token, each token routed to its own experts above
+    # dominant kernel: top-k + gate/up GEMVs + SwiGLU of the 10 selected
+    # experts, one launch per token; each token has its own scratch holding
+    # its own router logits, so every launch streams that token's experts
+    sb_tok = scratch.numel()
+    scr = torch.zeros(T, sb_tok, dtype=torch.uint8, device="cuda")
+    rb2 = RouteBuffers.alloc(T, w.top_k, w.n_experts, with_logits=False)
+    outs2 = [B.route_out(rb2.ids[t], rb2.weights[t], rb2.slots[t], rb2.miss_count[0:1],
+                         rb2.early_out[0:1]) for t in range(T)]
+    with torch.cuda.stream(stream):
+        st = stream.cuda_stream
+        for t in range(T):
+            B.rl_decode_stage(d, 0, 0, X[t], model.router[0], None, model.residency, model.pool,
+                              outs2[t], scr[t], sb_tok, Y[t], st)
+
     def gateup_all():
         st = torch.cuda.current_stream().cuda_stream
         for t in range(T):
-            lib.rl_decode_stage(C.byref(d), 1, xp[t], pool, C.byref(outs[t]), sp, sb, None, st)
+            lib.rl_decode_stage(C.byref(d), 1, 0, xp[t], W0, None, res, pool, C.byref(outs2[t]),
+                                scr[t].data_ptr(), sb_tok, None, st)
 
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -138,7 +151,9 @@ def main():
     with torch.cuda.stream(stream):
         gu_ms = event_ms(g2.replay, stream, 5) / T
     tb = B.rl_tensor_bytes(d)
-    gu_bytes = w.top_k * 2 * tb + w.hidden * 4 + w.top_k * w.width * 4
+    # codes of the 10 experts' gate and up tensors, x, logits, residency row, h
+    gu_bytes = (w.top_k * 2 * tb + w.hidden * 4 + w.n_experts * 4 * 2
+                + w.top_k * w.width * 4)
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     layer_bytes = w.top_k * 3 * tb + w.n_experts * w.hidden * 4 + 2 * w.hidden * 4
 
@@ -166,7 +181,7 @@ def main():
             "eager_us_per_token": round(eager_ms * 1e3 / T, 3),
         },
         "roofline": {
-            "kernel": "decode_gateup_kernel<2,64>",
+            "kernel": "decode_topk_gateup_kernel<8,2,64>",
             "bound": "hbm",
             "achieved": round(gu_gbs, 1),
             "peak": PEAK_HBM_GBS,

@@ -95,9 +95,9 @@ int64_t rl_tensor_bytes(const rl_moe_desc* d);
 int64_t rl_slot_bytes(const rl_moe_desc* d);
 
 /* Scratch sizes in bytes (negative = error code for a bad descriptor).
- * Scratch must be 256-byte aligned and zero-filled before its first use;
- * every call leaves its synchronisation words at zero again, so one zeroed
- * buffer serves any number of calls on one stream. */
+ * Scratch must be 256-byte aligned; its contents need no initialisation and
+ * are overwritten by every call (except where a stage entry point below
+ * reads what an earlier stage left there). */
 int64_t rl_route_scratch_bytes(const rl_moe_desc* d, int32_t n_tokens);
 int64_t rl_decode_scratch_bytes(const rl_moe_desc* d);
 int64_t rl_prefill_scratch_bytes(const rl_moe_desc* d, int32_t max_tokens);
@@ -178,16 +178,19 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
 
 /* Stage entry points, for tests and benchmarks: each enqueues the kernels of
  * one step of a path above, with the same arguments and scratch layout.
- *   rl_decode_stage: stage 1 = gate/up GEMVs + SwiGLU of the k selected
- *     experts (needs `route` filled by rl_route for this token; h goes to
- *     scratch); stage 2 = down GEMVs + rank-ordered sum into y (needs stage 1
- *     in the same scratch).  Same early-out behaviour as moe_decode_layer.
+ *   rl_decode_stage: stage 0 = router GEMV into scratch; stage 1 = softmax
+ *     top-k, lookup and flag (written to `route`) then the gate/up GEMVs +
+ *     SwiGLU of the k selected experts into scratch; stage 2 = down GEMVs +
+ *     rank-ordered sum into y.  Each stage needs the previous ones in the same
+ *     scratch.  Same early-out behaviour as moe_decode_layer.
  *   rl_prefill_stage: stage 0 = plan (needs `route` filled by rl_route for
  *     the n_tokens tokens of x), 1 = batched gate/up, 2 = batched down,
  *     3 = per-token ordered sum into y; each stage needs the previous ones in
  *     the same scratch (sized for n_tokens).
  * Sources as for moe_decode_layer (dev21, dev23) and moe_prefill_chunk (dev20). */
-int rl_decode_stage(const rl_moe_desc* d, int32_t stage, const float* x,
+int rl_decode_stage(const rl_moe_desc* d, int32_t stage, int32_t layer,
+                    const float* x, const float* router_w,
+                    const float* router_bias, const int32_t* residency,
                     const void* slot_pool, const rl_route_out* route,
                     void* scratch, int64_t scratch_bytes, float* y, void* stream);
 int rl_prefill_stage(const rl_moe_desc* d, int32_t stage, int32_t layer,

@@ -53,7 +53,8 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
                                     C.c_void_p]),
-    "rl_decode_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p, C.c_void_p,
+    "rl_decode_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
                                   C.c_void_p]),
     "rl_prefill_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
@@ -172,11 +173,12 @@ def moe_prefill_chunk(d, layer, n_tokens, plan_cap, x, router_w, router_bias, re
                  "moe_prefill_chunk")
 
 
-def rl_decode_stage(d, stage, x, slot_pool, route: RlRouteOut, scratch, scratch_bytes, y,
-                    stream=None) -> int:
-    return check(lib.rl_decode_stage(C.byref(d), stage, _ptr(x), _ptr(slot_pool), C.byref(route),
-                                     _ptr(scratch), scratch_bytes, _ptr(y), _stream(stream)),
-                 "rl_decode_stage")
+def rl_decode_stage(d, stage, layer, x, router_w, router_bias, residency, slot_pool,
+                    route: RlRouteOut, scratch, scratch_bytes, y, stream=None) -> int:
+    return check(lib.rl_decode_stage(C.byref(d), stage, layer, _ptr(x), _ptr(router_w),
+                                     _ptr(router_bias), _ptr(residency), _ptr(slot_pool),
+                                     C.byref(route), _ptr(scratch), scratch_bytes, _ptr(y),
+                                     _stream(stream)), "rl_decode_stage")
 
 
 def rl_prefill_stage(d, stage, layer, n_tokens, plan_cap, x, residency, slot_pool,

@@ -29,17 +29,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t a256(int64_t n) { return up256(n); }
 
-// --- decode / route scratch: logits [T*E] f32, counter u32, h [k*F] f32
+// --- decode / route scratch: logits [T*E] f32, h [k*F] f32
 struct DecodeLayout {
-  int64_t logits, counter, hbuf, total;
+  int64_t logits, hbuf, total;
 };
 DecodeLayout decode_layout(const rl_moe_desc* d, int T) {
   DecodeLayout l;
   int64_t off = 0;
   l.logits = off;
   off = a256(off + int64_t(T) * d->n_experts * 4);
-  l.counter = off;
-  off = a256(off + 4);
   l.hbuf = off;
   off = a256(off + int64_t(d->top_k) * d->width * 4);
   l.total = off;
@@ -109,7 +107,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVI
 
 RouteArgs route_args(const rl_moe_desc* d, int32_t layer, int32_t T, const float* x,
                      const float* router_w, const float* bias, const int32_t* residency,
-                     const rl_route_out* out, float* logits, uint32_t* counter) {
+                     const rl_route_out* out, float* logits) {
   RouteArgs a;
   a.x = x;
   a.W = router_w;
@@ -123,7 +121,6 @@ RouteArgs route_args(const rl_moe_desc* d, int32_t layer, int32_t T, const float
   a.residency = residency;
   a.logits = logits;
   a.logits_out = out->logits;
-  a.counter = counter;
   a.ids = out->ids;
   a.weights = out->weights;
   a.slots = out->slots;
@@ -132,17 +129,28 @@ RouteArgs route_args(const rl_moe_desc* d, int32_t layer, int32_t T, const float
   return a;
 }
 
-DecodeArgs decode_args(const rl_moe_desc* d, const float* x, const void* slot_pool,
+DecodeArgs decode_args(const rl_moe_desc* d, int32_t layer, const float* x, const float* router_w,
+                       const float* bias, const int32_t* residency, const void* slot_pool,
                        const rl_route_out* route, uint8_t* s, const DecodeLayout& l, float* y) {
   DecodeArgs da;
   da.pool = make_pool_view(slot_pool, d->hidden, d->width, d->qbits);
   da.H = d->hidden;
   da.F = d->width;
+  da.E = d->n_experts;
   da.k = d->top_k;
   da.qbits = d->qbits;
+  da.layer = layer;
+  da.n_slots = d->n_slots;
   da.x = x;
-  da.slots = route->slots;
+  da.W = router_w;
+  da.bias = bias;
+  da.residency = residency;
+  da.logits = reinterpret_cast<float*>(s + l.logits);
+  da.logits_out = route->logits;
+  da.ids = route->ids;
   da.weights = route->weights;
+  da.slots = route->slots;
+  da.miss_count = route->miss_count;
   da.early_out = route->early_out;
   da.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   da.y = y;
@@ -261,8 +269,7 @@ int rl_route(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, const float*
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
   uint8_t* s = static_cast<uint8_t*>(scratch);
   const RouteArgs a = route_args(d, layer, n_tokens, x, router_w, router_bias, residency, out,
-                                 reinterpret_cast<float*>(s + l.logits),
-                                 reinterpret_cast<uint32_t*>(s + l.counter));
+                                 reinterpret_cast<float*>(s + l.logits));
   launch_route(a, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -278,11 +285,9 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x, const 
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
   uint8_t* s = static_cast<uint8_t*>(scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const RouteArgs a = route_args(d, layer, 1, x, router_w, router_bias, residency, route,
-                                 reinterpret_cast<float*>(s + l.logits),
-                                 reinterpret_cast<uint32_t*>(s + l.counter));
-  launch_route(a, st);
-  const DecodeArgs da = decode_args(d, x, slot_pool, route, s, l, y);
+  const DecodeArgs da = decode_args(d, layer, x, router_w, router_bias, residency, slot_pool,
+                                    route, s, l, y);
+  launch_decode_router(da, st);
   launch_decode_gateup(da, st);
   launch_decode_down_sum(da, st);
   return launch_status();
@@ -301,7 +306,7 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int
   uint8_t* s = static_cast<uint8_t*>(scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const RouteArgs ra = route_args(d, layer, n_tokens, x, router_w, router_bias, residency, route,
-                                  reinterpret_cast<float*>(s + l.logits), nullptr);
+                                  reinterpret_cast<float*>(s + l.logits));
   launch_route(ra, st);
   const PrefillArgs a = prefill_args(d, layer, n_tokens, plan_cap, x, residency, slot_pool, route,
                                      s, l, y);
@@ -312,23 +317,23 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int
   return launch_status();
 }
 
-int rl_decode_stage(const rl_moe_desc* d, int32_t stage, const float* x, const void* slot_pool,
-                    const rl_route_out* route, void* scratch, int64_t scratch_bytes, float* y,
-                    void* stream) {
-  int rc = check_desc(d);
+int rl_decode_stage(const rl_moe_desc* d, int32_t stage, int32_t layer, const float* x,
+                    const float* router_w, const float* router_bias, const int32_t* residency,
+                    const void* slot_pool, const rl_route_out* route, void* scratch,
+                    int64_t scratch_bytes, float* y, void* stream) {
+  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
   if (rc) return rc;
-  rc = check_route_out(route);
-  if (rc) return rc;
-  if (!slot_pool || !scratch || !aligned(slot_pool, 256) || !aligned(scratch, 256))
-    return RL_E_INVAL;
-  if (stage == 1 && (!x || !aligned(x, 16))) return RL_E_INVAL;
+  if (!slot_pool || !aligned(slot_pool, 256)) return RL_E_INVAL;
   if (stage == 2 && (!y || !aligned(y, 16))) return RL_E_INVAL;
-  if (stage != 1 && stage != 2) return RL_E_RANGE;
+  if (stage < 0 || stage > 2) return RL_E_RANGE;
   const DecodeLayout l = decode_layout(d, 1);
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
-  const DecodeArgs da = decode_args(d, x, slot_pool, route, static_cast<uint8_t*>(scratch), l, y);
+  const DecodeArgs da = decode_args(d, layer, x, router_w, router_bias, residency, slot_pool,
+                                    route, static_cast<uint8_t*>(scratch), l, y);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (stage == 1)
+  if (stage == 0)
+    launch_decode_router(da, st);
+  else if (stage == 1)
     launch_decode_gateup(da, st);
   else
     launch_decode_down_sum(da, st);

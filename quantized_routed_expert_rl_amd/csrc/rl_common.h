@@ -159,11 +159,36 @@ __device__ inline uint32_t wave_reduce_u32(uint32_t v) {
 __device__ inline uint32_t wave_max_u32(uint32_t v) { return wave_reduce_u32<true>(v); }
 __device__ inline uint32_t wave_min_u32(uint32_t v) { return wave_reduce_u32<false>(v); }
 
+// DPP sum over groups of W consecutive lanes (W = 1..64, a power of two);
+// the group's total lands in its last lane (other lanes hold partial sums).
+// Lanes without a DPP source contribute 0 (bound_ctrl).
+template <int CTRL, int ROWMASK>
+__device__ inline float dpp_add(float x) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, true);
+  return x + __int_as_float(o);
+}
+
+template <int W>
+__device__ inline float group_sum_last(float v) {
+  if (W >= 2) v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+  if (W >= 4) v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+  if (W >= 8) v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+  if (W >= 16) v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+  if (W >= 32) v = dpp_add<0x142, 0xa>(v);  // row_bcast:15
+  if (W >= 64) v = dpp_add<0x143, 0xc>(v);  // row_bcast:31
+  return v;
+}
+
 // Order-preserving map of a float32 to uint32 (larger float -> larger key);
 // -0 is first folded to +0 so the two compare equal.
 __device__ inline uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_key (a -0 comes back as +0).
+__device__ inline float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }

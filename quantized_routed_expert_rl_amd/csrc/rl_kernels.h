@@ -16,7 +16,6 @@ struct RouteArgs {
   const int32_t* residency;
   float* logits;       // [T][E] scratch
   float* logits_out;   // optional copy for the caller
-  uint32_t* counter;   // T == 1 only: zeroed scratch word, left at zero
   int32_t* ids;
   float* weights;
   int32_t* slots;
@@ -27,14 +26,22 @@ void launch_route(const RouteArgs& a, hipStream_t st);
 
 struct DecodeArgs {
   PoolView pool;
-  int H, F, k, qbits;
+  int H, F, E, k, qbits, layer, n_slots;
   const float* x;
-  const int32_t* slots;
-  const float* weights;
-  const uint32_t* early_out;
-  float* hbuf;         // [k][F] scratch
+  const float* W;
+  const float* bias;
+  const int32_t* residency;
+  float* logits;        // [E] scratch
+  float* logits_out;    // optional copy for the caller
+  int32_t* ids;         // route outputs
+  float* weights;
+  int32_t* slots;
+  uint32_t* miss_count;
+  uint32_t* early_out;
+  float* hbuf;          // [k][F] scratch
   float* y;
 };
+void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);
 void launch_decode_down_sum(const DecodeArgs& a, hipStream_t st);
 

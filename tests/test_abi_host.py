@@ -34,7 +34,7 @@ def test_size_queries_match_format():
         assert B.rl_slot_bytes(d) == synth.slot_nbytes(H, F, qb)
     d = B.desc(2048, 512, 10, 512, 1, 2, 512)
     assert B.rl_slot_bytes(d) == 860_160
-    assert B.rl_decode_scratch_bytes(d) > 512 * 4 + 10 * 512 * 4
+    assert B.rl_decode_scratch_bytes(d) >= 512 * 4 + 10 * 512 * 4
     # prefill scratch holds at least the pair intermediates
     assert B.rl_prefill_scratch_bytes(d, 512) >= 5120 * (2048 + 512) * 4
     lay = B.rl_prefill_plan_layout(d, 512)
