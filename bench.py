@@ -35,7 +35,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB three times (the known-size "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def stored_traffic(tag):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from
+    profiles/traffic_<tag>.md, or None when the file is missing or the
+    kernel's sources no longer hash to the value the counters were taken at."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        k, sep, v = line.strip().partition(": ")
+        if sep and k in ("sources", "source_sha256", "fetch_bytes", "write_bytes"):
+            kv[k] = v.strip()
+    if len(kv) < 4:
+        return None
+    h = hashlib.sha256()
+    for src in kv["sources"].split(","):
+        f = os.path.join(ROOT, src)
+        if not os.path.exists(f):
+            return None
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != kv["source_sha256"]:
+        return None
+    return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
 
 
 def event_ms(fn, stream, reps):
@@ -69,6 +98,13 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     lib = B.lib
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------ decode
     w = workloads.get("decode_1l")
@@ -187,7 +223,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic("decode_topk_gateup"),
             "bytes_per_launch": gu_bytes,
             "us_per_launch": round(gu_ms * 1e3, 3),
         },
@@ -233,9 +269,13 @@ def main():
                        "chunk_frac_of_hbm": round(chunk_bytes / (p_ms * 1e-3) / 1e9
                                                   / PEAK_HBM_GBS, 4)},
             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-            "roofline": {"kernel": f"prefill_{dom}_kernel", "bound": "hbm",
+            "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_proj_mfma_kernel<true>",
+                                    "down": "quantize_rows_kernel<false> + prefill_proj_mfma_kernel<false>"
+                                    }[dom] if B.lib.rl_slot_bytes and w3.qbits == 2 else f"prefill {dom} stage",
+                         "bound": "hbm",
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": stored_traffic("prefill_" + dom),
                          "bytes_per_launch": gb[dom]},
         }
 
