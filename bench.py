@@ -271,7 +271,7 @@ def main():
             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
             "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_proj_mfma_kernel<true>",
                                     "down": "quantize_rows_kernel<false> + prefill_proj_mfma_kernel<false>"
-                                    }[dom] if B.lib.rl_slot_bytes and w3.qbits == 2 else f"prefill {dom} stage",
+                                    }[dom] if w3.qbits == 2 and w3.width % 256 == 0 else f"prefill {dom} stage",
                          "bound": "hbm",
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_GBS, 4),
