@@ -217,7 +217,8 @@ def main():
             "eager_us_per_token": round(eager_ms * 1e3 / T, 3),
         },
         "roofline": {
-            "kernel": "decode_topk_gateup_kernel<8,2,64>",
+            "kernel": ("decode_topk_gateup_mfma_kernel<8, 8>" if w.qbits == 2 and w.width % 256 == 0
+                       else "decode_topk_gateup_kernel<8, 2, 64>"),
             "bound": "hbm",
             "achieved": round(gu_gbs, 1),
             "peak": PEAK_HBM_GBS,

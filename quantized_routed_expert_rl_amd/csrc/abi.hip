@@ -154,6 +154,7 @@ DecodeArgs decode_args(const rl_moe_desc* d, int32_t layer, const float* x, cons
   da.early_out = route->early_out;
   da.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   da.y = y;
+  da.mfma = d->qbits == 2 && d->width % 256 == 0;
   return da;
 }
 

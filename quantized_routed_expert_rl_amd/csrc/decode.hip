@@ -255,6 +255,10 @@ static void gateup_n(const DecodeArgs& a, hipStream_t st) {
 }
 
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st) {
+  if (a.mfma) {
+    launch_decode_gateup_mfma(a, st);
+    return;
+  }
   switch (cand_per_lane(a.E)) {
     case 1: gateup_n<1>(a, st); break;
     case 2: gateup_n<2>(a, st); break;
@@ -291,6 +295,10 @@ static void down_q(const DecodeArgs& a, hipStream_t st) {
 }
 
 void launch_decode_down_sum(const DecodeArgs& a, hipStream_t st) {
+  if (a.mfma) {
+    launch_decode_down_sum_mfma(a, st);
+    return;
+  }
   if (a.qbits == 3) down_q<3>(a, st); else down_q<2>(a, st);
 }
 

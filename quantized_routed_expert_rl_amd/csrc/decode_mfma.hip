@@ -1,0 +1,344 @@
+// Single-token decode expert GEMVs on the int8 matrix cores of gfx950, for
+// the 2-bit block format when the expert width is a multiple of 256 (the
+// operands are described in rl_mfma.h).  Same three-kernel structure and
+// routing rules as decode.hip ("Red Lite dev21 - GPU-routed decode", "What
+// changed"; "Red Lite dev23", "What changed": with the flag set every expert
+// kernel returns at once; "Red Lite dev20", "What changed": a token's experts
+// are summed in router selection order).
+//
+// Diagonal tiles.  A GEMV has one activation vector, so of the 16 columns of
+// an MFMA only the 4 digit columns would carry data.  Instead a 16-row A tile
+// holds RPT = 16/BPT output rows times BPT 256-value K-blocks (A row
+// rho = BPT*i + beta), and B column c = 4*beta' + digit holds the digits of
+// K-block beta'.  Output entry (rho, c) is wanted when beta == beta', i.e.
+// the diagonal 4x4 blocks; the rest is discarded.  Output lane l holds rows
+// 4*(l/16) + v, so every wanted entry of output row i sits in the 16-lane
+// group l/16 = BPT*i/4, and one DPP sum over that group finishes the row.
+#include "rl_common.h"
+#include "rl_kernels.h"
+#include "rl_mfma.h"
+#include "rl_select.h"
+
+namespace rl {
+
+int cand_per_lane(int E);
+
+__device__ inline int sel4(const v4i& D, int v) {
+  return v == 0 ? D.x : v == 1 ? D.y : v == 2 ? D.z : D.w;
+}
+
+// B operand of tile half h (K-blocks BPT*h .. BPT*h + BPT - 1) from the
+// digit operands of a vector (KB blocks of 1024 bytes in LDS).  Columns of
+// blocks beta' >= BPT are zero.
+template <int BPT>
+__device__ inline void load_b_diag(const uint8_t* xq, int h, int lane, v4i B[4]) {
+  const int c = lane & 15, beta = c >> 2, d = c & 3, q = lane >> 4;
+  const bool ok = beta < BPT;
+  const uint8_t* base = xq + ((ok ? beta : 0) + BPT * h) * 1024;
+  const int msk = ok ? -1 : 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int4 v = *reinterpret_cast<const int4*>(base + digit_chunk_offset(q, d, m));
+    B[m] = v4i{v.x & msk, v.y & msk, v.z & msk, v.w & msk};
+  }
+}
+
+// Adds the wanted entries of one tile half's int32 result D, scaled to
+// float, into acc[il] (output row 4*(lane/16)/BPT + il of the tile).
+// dh: the lane's block scale bits from its A tile; xe: exponents of the
+// vector's K-blocks.
+template <int BPT>
+__device__ inline void diag_accumulate(const v4i& D, uint32_t dh, const int* xe, int h, int lane,
+                                       float* acc) {
+  constexpr int RG = 4 / BPT;
+  const int g = lane >> 4, c = lane & 15, bc = c >> 2, dc = c & 3;
+  const bool useful = bc < BPT;
+  const int b = useful ? bc : 0;
+  const int sh = 8 * (3 - dc) - xe[b + BPT * h];
+#pragma unroll
+  for (int il = 0; il < RG; ++il) {
+    const int v = BPT * il + b;
+    // block scale of A row 4g + v, held by A lane 4g + v (quad 0)
+    const float dq = dh_dq(uint32_t(__shfl(int(dh), 4 * g + v, kWave)));
+    const float t = float(sel4(D, v)) * ldexpf(dq, sh);
+    acc[il] += useful ? t : 0.f;
+  }
+}
+
+// One 16-value run of a vector (K = 16*run .. +15) -> its four digit chunks
+// in LDS, with one exponent per 256-value block.  The 16 runs of a block
+// must sit in 16 consecutive lanes starting at a multiple of 16, all of
+// which call this (act = false for lanes past the end).
+__device__ inline void quantize_run(const float* __restrict__ src, int run, bool act, uint8_t* xq,
+                                    int* xe) {
+  const int k0 = 16 * (act ? run : 0);
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 f = *reinterpret_cast<const float4*>(src + k0 + 4 * u);
+    v[4 * u + 0] = f.x;
+    v[4 * u + 1] = f.y;
+    v[4 * u + 2] = f.z;
+    v[4 * u + 3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) amax = fmaxf(amax, fabsf(v[n]));
+  if (!act) amax = 0.f;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const int e = scale_exp(amax);
+  if (act) {
+    uint4 ch[4];
+    digit_chunks(v, e, ch);
+    const int kb = k0 >> 8, qq = (k0 & 255) >> 6, mm = (k0 & 63) >> 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      *reinterpret_cast<uint4*>(xq + kb * 1024 + digit_chunk_offset(qq, d, mm)) = ch[d];
+    if ((k0 & 255) == 0) xe[kb] = e;
+  }
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// -------------------------------------------------- top-k + gate/up
+// Grid: k * F/(4*RPT) work blocks + 1 publisher block, 4 waves each.
+// Every block selects the experts (wave 0) while waves 1-3 turn x into digit
+// operands in LDS.  The publisher computes the renormalised weights and
+// writes ids, weights, slots, the miss count and the flag; a work block only
+// looks up its slots.  Work block = (rank r, 4*RPT rows j); wave w takes
+// RPT rows of gate and up over all KB = H/256 K-blocks: 2*NH diagonal tiles.
+template <int N, int KB>
+__global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
+    PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
+    const float* __restrict__ x, const float* __restrict__ logits,
+    const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
+    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf) {
+  constexpr int BPT = KB < 4 ? KB : 4;   // K-blocks per tile
+  constexpr int RPT = 16 / BPT;          // output rows per tile
+  constexpr int NH = KB / BPT;           // tiles per tensor
+  constexpr int RG = 4 / BPT;            // output rows per 16-lane group
+  __shared__ int s_res[1024];
+  __shared__ __align__(16) uint32_t s_key[64 * N];
+  __shared__ __align__(16) int s_idx[64 * N];
+  __shared__ int sel_ids[32];
+  __shared__ float sel_lg[32];
+  __shared__ int s_slot[32];
+  __shared__ int s_miss;
+  __shared__ __align__(16) uint8_t s_xq[KB * 1024];
+  __shared__ int s_xe[KB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool publisher = blockIdx.x == gridDim.x - 1;
+  {  // residency row to LDS: E <= 1024, four unconditional (clamped) loads per thread
+    int rv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rv[u] = residency[int64_t(layer) * E + (tid + 256 * u < E ? tid + 256 * u : 0)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tid + 256 * u < E) s_res[tid + 256 * u] = rv[u];
+  }
+  if (wv == 0) {
+    wave_topk<N>(logits, E, k, s_key, s_idx, sel_ids, sel_lg);
+  } else if (!publisher) {
+    const int run = tid - 64;            // H/16 <= 128 runs over waves 1-2
+    quantize_run(x, run, run < H / 16, s_xq, s_xe);
+  }
+  __syncthreads();
+  if (publisher) {
+    if (wv == 0) {
+      const int miss = finish_token(sel_ids, sel_lg, k, E, n_slots, s_res, ids, weights, slots);
+      if (lane == 0) {
+        *miss_count = uint32_t(miss);
+        *early_out = miss > 0 ? 1u : 0u;
+      }
+    }
+    return;
+  }
+  if (wv == 0) {
+    int slot = -1;
+    if (lane < k) {
+      const int e = min(max(sel_ids[lane], 0), E - 1);
+      const int v = s_res[e];
+      slot = (v >= 0 && v < n_slots) ? v : -1;
+      s_slot[lane] = slot;
+    }
+    const int miss = __popcll(__ballot(lane < k && slot < 0));
+    if (lane == 0) s_miss = miss;
+  }
+  __syncthreads();
+  if (s_miss) return;                    // early-out: nothing downstream runs
+  const int jpb = 4 * RPT;
+  const int bpr = F / jpb;
+  const int r = blockIdx.x / bpr;
+  const int j0 = (blockIdx.x % bpr) * jpb + wv * RPT;
+  const int slot = s_slot[r];
+  const uint8_t* tg = tensor_base(pv, slot, 0);
+  const uint8_t* tu = tensor_base(pv, slot, 1);
+  const int rho = lane & 15, q = lane >> 4;
+  const int64_t blk = int64_t(j0 + rho / BPT) * KB + rho % BPT;
+  TileCodes cg[NH], cu[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    cg[h] = load_tile(tg, pv, blk + BPT * h, q);
+    cu[h] = load_tile(tu, pv, blk + BPT * h, q);
+  }
+  float ag[RG], au[RG];
+#pragma unroll
+  for (int il = 0; il < RG; ++il) ag[il] = au[il] = 0.f;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    v4i B[4], A[4];
+    load_b_diag<BPT>(s_xq, h, lane, B);
+    dequant_tile(cg[h], A);
+    const v4i Dg = mfma4(A, B);
+    dequant_tile(cu[h], A);
+    const v4i Du = mfma4(A, B);
+    diag_accumulate<BPT>(Dg, cg[h].dh, s_xe, h, lane, ag);
+    diag_accumulate<BPT>(Du, cu[h].dh, s_xe, h, lane, au);
+  }
+#pragma unroll
+  for (int il = 0; il < RG; ++il) {
+    ag[il] = group_sum_last<16>(ag[il]);
+    au[il] = group_sum_last<16>(au[il]);
+  }
+  if ((lane & 15) == 15) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int il = 0; il < RG; ++il)
+      hbuf[int64_t(r) * F + j0 + g * RG + il] = silu_mul(ag[il], au[il]);
+  }
+}
+
+// ------------------------------------------------- down + ordered sum
+// Block = RPT output rows i for all k experts; one wave per expert (up to
+// the wave count; more experts loop).  A wave turns h_r into digit operands
+// in its own LDS region while its down codes load, runs NH diagonal tiles,
+// and leaves e_r[i] in LDS; then y[i] = fma(w_r, e_r[i], acc), r = 0..k-1.
+// Dynamic LDS: nw * (KBD*1024 + KBD*4) + k*RPT*4 bytes.
+template <int KBD>
+__global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
+    PoolView pv, int H, int F, int k, const int32_t* __restrict__ slots,
+    const float* __restrict__ weights, const float* __restrict__ hbuf,
+    const uint32_t* __restrict__ early_out, float* __restrict__ y) {
+  constexpr int BPT = KBD < 4 ? KBD : 4;
+  constexpr int RPT = 16 / BPT;
+  constexpr int NH = KBD / BPT;
+  constexpr int RG = 4 / BPT;
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint8_t* s_hq = s_dyn + wv * KBD * 1024;
+  int* s_he = reinterpret_cast<int*>(s_dyn + nw * KBD * 1024) + wv * KBD;
+  float* s_e = reinterpret_cast<float*>(s_dyn + nw * KBD * 1024 + nw * KBD * 4);
+  // the flag and the first expert's slot are loaded together; only the code
+  // loads (whose addresses need a valid slot) wait for the flag
+  const uint32_t flag = *early_out;
+  int slot_next = slots[wv < k ? wv : 0];
+  if (flag) return;
+  const int i0 = blockIdx.x * RPT;
+  const int rho = lane & 15, q = lane >> 4;
+  const int64_t blk = int64_t(i0 + rho / BPT) * KBD + rho % BPT;
+  for (int r = wv; r < k; r += nw) {
+    const int slot = slot_next;
+    if (r + nw < k) slot_next = slots[r + nw];
+    const uint8_t* td = tensor_base(pv, slot, 2);
+    TileCodes cd[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) cd[h] = load_tile(td, pv, blk + BPT * h, q);
+    const float* hr = hbuf + int64_t(r) * F;
+#pragma unroll
+    for (int u = 0; u < (16 * KBD + 63) / 64; ++u) {
+      const int run = lane + 64 * u;
+      quantize_run(hr, run, run < 16 * KBD, s_hq, s_he);
+    }
+    wave_lds_sync();
+    float acc[RG];
+#pragma unroll
+    for (int il = 0; il < RG; ++il) acc[il] = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      v4i B[4], A[4];
+      load_b_diag<BPT>(s_hq, h, lane, B);
+      dequant_tile(cd[h], A);
+      const v4i D = mfma4(A, B);
+      diag_accumulate<BPT>(D, cd[h].dh, s_he, h, lane, acc);
+    }
+#pragma unroll
+    for (int il = 0; il < RG; ++il) acc[il] = group_sum_last<16>(acc[il]);
+    if ((lane & 15) == 15) {
+      const int g = lane >> 4;
+#pragma unroll
+      for (int il = 0; il < RG; ++il) s_e[r * RPT + g * RG + il] = acc[il];
+    }
+    wave_lds_sync();                     // digit region reused by the next expert
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < RPT; t += blockDim.x) {
+    float a = 0.f;
+    for (int r = 0; r < k; ++r) a = fmaf(weights[r], s_e[r * RPT + t], a);
+    y[i0 + t] = a;
+  }
+}
+
+// ------------------------------------------------------------ launchers
+template <int N, int KB>
+static void gateup_mfma(const DecodeArgs& a, hipStream_t st) {
+  constexpr int BPT = KB < 4 ? KB : 4;
+  const int blocks = a.k * (a.F / (4 * (16 / BPT))) + 1;
+  decode_topk_gateup_mfma_kernel<N, KB><<<blocks, 256, 0, st>>>(
+      a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
+      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf);
+}
+
+template <int N>
+static void gateup_mfma_n(const DecodeArgs& a, hipStream_t st) {
+  switch (a.H / 256) {
+    case 1: gateup_mfma<N, 1>(a, st); break;
+    case 2: gateup_mfma<N, 2>(a, st); break;
+    case 4: gateup_mfma<N, 4>(a, st); break;
+    default: gateup_mfma<N, 8>(a, st); break;
+  }
+}
+
+void launch_decode_gateup_mfma(const DecodeArgs& a, hipStream_t st) {
+  switch (cand_per_lane(a.E)) {
+    case 1: gateup_mfma_n<1>(a, st); break;
+    case 2: gateup_mfma_n<2>(a, st); break;
+    case 4: gateup_mfma_n<4>(a, st); break;
+    case 8: gateup_mfma_n<8>(a, st); break;
+    default: gateup_mfma_n<16>(a, st); break;
+  }
+}
+
+// Waves per down block: one per expert, at most 16, and few enough that the
+// digit regions fit in 64 KiB of LDS.
+int decode_down_mfma_waves(int k, int F) {
+  const int kbd = F / 256;
+  int nw = k < 16 ? k : 16;
+  const int cap = (60 * 1024) / (kbd * 1028);
+  return nw < cap ? nw : cap;
+}
+
+template <int KBD>
+static void down_mfma(const DecodeArgs& a, hipStream_t st) {
+  constexpr int BPT = KBD < 4 ? KBD : 4;
+  constexpr int RPT = 16 / BPT;
+  const int nw = decode_down_mfma_waves(a.k, a.F);
+  const size_t lds = size_t(nw) * (KBD * 1024 + KBD * 4) + size_t(a.k) * RPT * 4;
+  decode_down_sum_mfma_kernel<KBD><<<a.H / RPT, 64 * nw, lds, st>>>(
+      a.pool, a.H, a.F, a.k, a.slots, a.weights, a.hbuf, a.early_out, a.y);
+}
+
+void launch_decode_down_sum_mfma(const DecodeArgs& a, hipStream_t st) {
+  switch (a.F / 256) {
+    case 1: down_mfma<1>(a, st); break;
+    case 2: down_mfma<2>(a, st); break;
+    case 4: down_mfma<4>(a, st); break;
+    default: down_mfma<8>(a, st); break;
+  }
+}
+
+}  // namespace rl

@@ -4,46 +4,17 @@
 // ingestion", "What changed": batched gate/up and down over (expert, token)
 // pairs sorted by expert).
 //
-// Exactness.  A 2-bit weight is d * q / 32 with the integer q = (2s+1)(2c-3)
-// in [-93, 93]: an int8, turned out of the code bits by one byte permute
-// against a 4-entry table per group.  An activation row is scaled by a power
-// of two 2^e (per row, or per 256-value block) so that |x * 2^e| < 2^30,
-// rounded to the integer X, and X is written as four balanced base-256 digits
-// in [-128, 127].  Each MFMA then sums int8 * int8 products exactly in int32
-// over one 256-value block (|sum| < 2^22), and the block's int32 result is
-// scaled by d/32 and 2^(8*(3-digit) - e) into a float32 accumulator.  Values
-// with |x| >= 2^-7 max|x| are represented exactly; the rest lose nothing
-// above 2^-31 max|x|.
-//
-// Operand layout (checked on the device): A lane l holds row l%16 and the 16
-// bytes of K-slice l/16; B lane l holds column l%16 and the same K-slice; the
-// output lane l holds rows 4*(l/16)+v, v < 4, of column l%16.  Inside a
-// 256-value block, lane quad q and MFMA m cover K = 64q + 16m + [0, 16), and
-// byte i of dword jj of the operand is K offset 4i + jj (the order in which
-// (codes >> 2jj) & 0x03030303 exposes four codes).  Columns are
-// 4 * token + digit.
+// The int8 operands and their exactness are described in rl_mfma.h; columns
+// of the B operand are 4 * token + digit.
 #include "rl_common.h"
 #include "rl_kernels.h"
+#include "rl_mfma.h"
 
 namespace rl {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 12;   // tokens per token tile: 3 column tiles of 4 tokens x 4 digits
 
 // --------------------------------------------------------------- digits
-// e with max * 2^e < 2^30 (0 for a zero or non-finite max).
-__device__ inline int scale_exp(float amax) {
-  if (!(amax > 0.f) || !(amax < 3.0e38f)) return 0;
-  int E;
-  frexpf(amax, &E);
-  return 30 - E;
-}
-
-// Balanced base-256 digits of X (|X| <= 2^30): digit d (0 = most significant)
-// in byte 3-d, as a two's complement int8.
-__device__ inline uint32_t digits_of(int X) { return (uint32_t(X) + 0x80808080u) ^ 0x80808080u; }
-
 // Rows of K float32 values -> operand-ready digit bytes.  Row r goes to
 // q + r*K*4; the 16-byte chunk of (block kb, quad qq, digit d) starts at
 // ((kb*4 + qq)*4 + d)*64 and holds MFMA m's 16 bytes at m*16.  Exponents:
@@ -87,78 +58,14 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   __syncthreads();
   if (!active) return;
   const int e = scale_exp(__uint_as_float(s_max[grp]));
-  uint32_t Z[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) Z[n] = digits_of(int(rintf(ldexpf(v[n], e))));
+  uint4 ch[4];
+  digit_chunks(v, e, ch);
   const int kb = k0 >> 8, qq = (k0 & 255) >> 6, mm = (k0 & 63) >> 4;
-  uint8_t* row = q + int64_t(r) * K * 4;
+  uint8_t* row = q + int64_t(r) * K * 4 + kb * 1024;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t b = 3 - d;   // byte of digit d in Z
-    uint32_t w[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      // bytes i = 0..3 <- Z[4i + jj] byte b
-      const uint32_t lo = __builtin_amdgcn_perm(Z[4 + jj], Z[jj], b | ((b + 4) << 8));
-      const uint32_t hi = __builtin_amdgcn_perm(Z[12 + jj], Z[8 + jj], b | ((b + 4) << 8));
-      w[jj] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-    *reinterpret_cast<uint4*>(row + ((kb * 4 + qq) * 4 + d) * 64 + mm * 16) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  for (int d = 0; d < 4; ++d)
+    *reinterpret_cast<uint4*>(row + digit_chunk_offset(qq, d, mm)) = ch[d];
   if ((k0 & 255) == 0) ex[int64_t(r) * (K >> 8) + kb] = e;
-}
-
-// ------------------------------------------------------------- weights
-// Byte table of q = (2s+1)(2c-3) for c = 0..3: {-3m, -m, m, 3m}, m = 2s+1.
-__device__ inline uint32_t lut2(uint32_t s) {
-  const uint32_t m = 2u * s + 1u;
-  return ((0x10100u - 259u * m) & 0xffffu) | ((m * 0x0301u) << 16);
-}
-
-__device__ inline v4i dequant_dword(uint32_t w, uint32_t lut) {
-  v4i a;
-  a.x = int(__builtin_amdgcn_perm(lut, lut, w & 0x03030303u));
-  a.y = int(__builtin_amdgcn_perm(lut, lut, (w >> 2) & 0x03030303u));
-  a.z = int(__builtin_amdgcn_perm(lut, lut, (w >> 4) & 0x03030303u));
-  a.w = int(__builtin_amdgcn_perm(lut, lut, (w >> 6) & 0x03030303u));
-  return a;
-}
-
-// One lane's share of a 16-row x 256-column block tile of a tensor.
-// Raw bytes only: nothing is computed from a load when it is issued, so a
-// prefetched tile does not make the wave wait.
-struct TileCodes {
-  uint4 c;       // 64 codes: K = 64q .. 64q+63 of the block, row l%16
-  uint32_t s;    // group scales of groups 2q (low nibble) and 2q+1
-  uint32_t dh;   // block scale d of the lane's row, binary16 bits
-};
-
-__device__ inline TileCodes load_tile(const uint8_t* t, const PoolView& p, int64_t blk, int q) {
-  TileCodes r;
-  r.c = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 16 * q);
-  r.s = t[p.s + 4 * blk + q];
-  r.dh = *reinterpret_cast<const uint16_t*>(t + p.d + 2 * blk);
-  return r;
-}
-
-__device__ inline float tile_dq(const TileCodes& t) {
-  return half_bits_to_float(uint16_t(t.dh)) * (1.f / 32.f);
-}
-
-__device__ inline void dequant_tile(const TileCodes& tc, v4i A[4]) {
-  const uint32_t l0 = lut2(tc.s & 15u), l1 = lut2(tc.s >> 4);
-  A[0] = dequant_dword(tc.c.x, l0);
-  A[1] = dequant_dword(tc.c.y, l0);
-  A[2] = dequant_dword(tc.c.z, l1);
-  A[3] = dequant_dword(tc.c.w, l1);
-}
-
-__device__ inline v4i mfma4(const v4i A[4], const v4i B[4]) {
-  v4i D = {0, 0, 0, 0};
-#pragma unroll
-  for (int m = 0; m < 4; ++m) D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[m], B[m], D, 0, 0, 0);
-  return D;
 }
 
 // -------------------------------------------------- batched projections

@@ -40,10 +40,13 @@ struct DecodeArgs {
   uint32_t* early_out;
   float* hbuf;          // [k][F] scratch
   float* y;
+  bool mfma;            // int8 matrix-core expert kernels (2-bit, F % 256 == 0)
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);
 void launch_decode_down_sum(const DecodeArgs& a, hipStream_t st);
+void launch_decode_gateup_mfma(const DecodeArgs& a, hipStream_t st);
+void launch_decode_down_sum_mfma(const DecodeArgs& a, hipStream_t st);
 
 // Plan of a prefill chunk inside scratch (see rl_prefill_layout).
 struct PlanPtrs {
