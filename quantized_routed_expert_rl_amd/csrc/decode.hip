@@ -83,8 +83,8 @@ __global__ __launch_bounds__(64) void decode_router_kernel(
 
 // -------------------------------------------------- 2. top-k + gate/up
 // Block = (expert rank r, 16 rows j); wave w takes rows j0+4w .. +3 of gate
-// and of up.  Wave 0 selects the experts while the other waves load x and
-// the residency row; block 0 publishes the routing results.
+// and of up.  Wave 0 selects the experts while the other waves load x;
+// block 0 publishes the routing results.
 template <int N, int QBITS, int LPR>
 __global__ __launch_bounds__(256) void decode_topk_gateup_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
@@ -94,32 +94,22 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_kernel(
   constexpr int RPI = 64 / LPR;     // rows per wave iteration
   constexpr int JW = 4;             // j values per wave
   constexpr int NIT = 2 * JW / RPI > 0 ? 2 * JW / RPI : 1;
-  __shared__ int s_res[1024];
-  __shared__ __align__(16) uint32_t s_key[64 * N];
-  __shared__ __align__(16) int s_idx[64 * N];
+  __shared__ __align__(16) TopkLds s_tk;
   __shared__ int sel_ids[32];
   __shared__ float sel_lg[32];
+  __shared__ int sel_res[32];
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
   __shared__ int s_slot[32];
   __shared__ int s_miss;
   __shared__ float s_row[4][2 * JW];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  {  // residency row to LDS: E <= 1024, four unconditional (clamped) loads per thread
-    int rv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rv[u] = residency[int64_t(layer) * E + (tid + 256 * u < E ? tid + 256 * u : 0)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (tid + 256 * u < E) s_res[tid + 256 * u] = rv[u];
-  }
   const int seg = lane % LPR, rs = lane / LPR;
   float xv[32], xsum;
   load_act32(x + 32 * seg, xv, xsum);
-  if (wv == 0) wave_topk<N>(logits, E, k, s_key, s_idx, sel_ids, sel_lg);
-  __syncthreads();
   if (wv == 0) {
-    const int miss = finish_token(sel_ids, sel_lg, k, E, n_slots, s_res, s_ids, s_w, s_slot);
+    wave_topk<N>(logits, E, k, residency + int64_t(layer) * E, s_tk, sel_ids, sel_lg, sel_res);
+    const int miss = finish_token(sel_ids, sel_lg, sel_res, k, E, n_slots, s_ids, s_w, s_slot);
     if (lane == 0) s_miss = miss;
     if (blockIdx.x == 0) {
       if (lane < k) {

@@ -65,14 +65,26 @@ __device__ inline void diag_accumulate(const v4i& D, uint32_t dh, const int* xe,
   }
 }
 
-// One 16-value run of a vector (K = 16*run .. +15) -> its four digit chunks
-// in LDS, with one exponent per 256-value block.  The 16 runs of a block
-// must sit in 16 consecutive lanes starting at a multiple of 16, all of
-// which call this (act = false for lanes past the end).
-__device__ inline void quantize_run(const float* __restrict__ src, int run, bool act, uint8_t* xq,
-                                    int* xe) {
+// Max over the 16 lanes of each DPP row, in every lane of the row (row_ror
+// by 1, 2, 4 and 8).
+template <int CTRL>
+__device__ inline float row_ror_max(float x) {
+  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+  return fmaxf(x, o);
+}
+__device__ inline float row_max16(float x) {
+  x = row_ror_max<0x121>(x);   // row_ror:1
+  x = row_ror_max<0x122>(x);   // row_ror:2
+  x = row_ror_max<0x124>(x);   // row_ror:4
+  x = row_ror_max<0x128>(x);   // row_ror:8
+  return x;
+}
+
+// One 16-value run of a vector (K = 16*run .. +15), loaded (lanes past the
+// end load run 0 and are ignored).
+__device__ __forceinline__ void load_run(const float* __restrict__ src, int run, bool act,
+                                         float* v) {
   const int k0 = 16 * (act ? run : 0);
-  float v[16];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const float4 f = *reinterpret_cast<const float4*>(src + k0 + 4 * u);
@@ -81,16 +93,22 @@ __device__ inline void quantize_run(const float* __restrict__ src, int run, bool
     v[4 * u + 2] = f.z;
     v[4 * u + 3] = f.w;
   }
+}
+
+// A loaded run -> its four digit chunks in LDS, with one exponent per
+// 256-value block.  The 16 runs of a block must sit in one DPP row (16
+// consecutive lanes starting at a multiple of 16), all of which call this.
+__device__ __forceinline__ void quantize_loaded(const float* v, int run, bool act, uint8_t* xq,
+                                                int* xe) {
   float amax = 0.f;
 #pragma unroll
   for (int n = 0; n < 16; ++n) amax = fmaxf(amax, fabsf(v[n]));
-  if (!act) amax = 0.f;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  amax = row_max16(act ? amax : 0.f);
   const int e = scale_exp(amax);
   if (act) {
     uint4 ch[4];
     digit_chunks(v, e, ch);
+    const int k0 = 16 * run;
     const int kb = k0 >> 8, qq = (k0 & 255) >> 6, mm = (k0 & 63) >> 4;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -99,18 +117,13 @@ __device__ inline void quantize_run(const float* __restrict__ src, int run, bool
   }
 }
 
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // -------------------------------------------------- top-k + gate/up
 // Grid: k * F/(4*RPT) work blocks + 1 publisher block, 4 waves each.
-// Every block selects the experts (wave 0) while waves 1-3 turn x into digit
-// operands in LDS.  The publisher computes the renormalised weights and
-// writes ids, weights, slots, the miss count and the flag; a work block only
-// looks up its slots.  Work block = (rank r, 4*RPT rows j); wave w takes
+// Every block selects the experts (wave 0, which loads the residency entries
+// of its experts with their logits) while waves 1-2 turn x into digit
+// operands in LDS; one barrier joins them.  The publisher computes the
+// renormalised weights and writes ids, weights, slots, the miss count and
+// the flag; a work block only needs its slots.  Work block = (rank r, 4*RPT rows j); wave w takes
 // RPT rows of gate and up over all KB = H/256 K-blocks: 2*NH diagonal tiles.
 template <int N, int KB>
 __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
@@ -122,53 +135,37 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
   constexpr int RPT = 16 / BPT;          // output rows per tile
   constexpr int NH = KB / BPT;           // tiles per tensor
   constexpr int RG = 4 / BPT;            // output rows per 16-lane group
-  __shared__ int s_res[1024];
-  __shared__ __align__(16) uint32_t s_key[64 * N];
-  __shared__ __align__(16) int s_idx[64 * N];
+  __shared__ __align__(16) TopkLds s_tk;
   __shared__ int sel_ids[32];
   __shared__ float sel_lg[32];
+  __shared__ int sel_res[32];
   __shared__ int s_slot[32];
   __shared__ int s_miss;
   __shared__ __align__(16) uint8_t s_xq[KB * 1024];
   __shared__ int s_xe[KB];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool publisher = blockIdx.x == gridDim.x - 1;
-  {  // residency row to LDS: E <= 1024, four unconditional (clamped) loads per thread
-    int rv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rv[u] = residency[int64_t(layer) * E + (tid + 256 * u < E ? tid + 256 * u : 0)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (tid + 256 * u < E) s_res[tid + 256 * u] = rv[u];
-  }
   if (wv == 0) {
-    wave_topk<N>(logits, E, k, s_key, s_idx, sel_ids, sel_lg);
-  } else if (!publisher) {
-    const int run = tid - 64;            // H/16 <= 128 runs over waves 1-2
-    quantize_run(x, run, run < H / 16, s_xq, s_xe);
-  }
-  __syncthreads();
-  if (publisher) {
-    if (wv == 0) {
-      const int miss = finish_token(sel_ids, sel_lg, k, E, n_slots, s_res, ids, weights, slots);
+    wave_topk<N>(logits, E, k, residency + int64_t(layer) * E, s_tk, sel_ids, sel_lg, sel_res);
+    if (publisher) {
+      const int miss = finish_token(sel_ids, sel_lg, sel_res, k, E, n_slots, ids, weights, slots);
       if (lane == 0) {
         *miss_count = uint32_t(miss);
         *early_out = miss > 0 ? 1u : 0u;
       }
+    } else {
+      const int slot = lane < k ? slot_of(sel_res[lane], n_slots) : 0;
+      if (lane < k) s_slot[lane] = slot;
+      const int miss = __popcll(__ballot(slot < 0));
+      if (lane == 0) s_miss = miss;
     }
-    return;
+  } else if (!publisher) {
+    const int run = tid - 64;            // H/16 <= 128 runs over waves 1-2
+    float v[16];
+    load_run(x, run, run < H / 16, v);
+    quantize_loaded(v, run, run < H / 16, s_xq, s_xe);
   }
-  if (wv == 0) {
-    int slot = -1;
-    if (lane < k) {
-      const int e = min(max(sel_ids[lane], 0), E - 1);
-      const int v = s_res[e];
-      slot = (v >= 0 && v < n_slots) ? v : -1;
-      s_slot[lane] = slot;
-    }
-    const int miss = __popcll(__ballot(lane < k && slot < 0));
-    if (lane == 0) s_miss = miss;
-  }
+  if (publisher) return;
   __syncthreads();
   if (s_miss) return;                    // early-out: nothing downstream runs
   const int jpb = 4 * RPT;
@@ -241,19 +238,23 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
   const int i0 = blockIdx.x * RPT;
   const int rho = lane & 15, q = lane >> 4;
   const int64_t blk = int64_t(i0 + rho / BPT) * KBD + rho % BPT;
+  constexpr int NU = (16 * KBD + 63) / 64;   // runs of 16 values per lane
   for (int r = wv; r < k; r += nw) {
+    // h_r first: its quantisation then overlaps the code loads (loads
+    // complete in issue order)
+    const float* hr = hbuf + int64_t(r) * F;
+    float v[NU][16];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load_run(hr, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
     const int slot = slot_next;
     if (r + nw < k) slot_next = slots[r + nw];
     const uint8_t* td = tensor_base(pv, slot, 2);
     TileCodes cd[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) cd[h] = load_tile(td, pv, blk + BPT * h, q);
-    const float* hr = hbuf + int64_t(r) * F;
 #pragma unroll
-    for (int u = 0; u < (16 * KBD + 63) / 64; ++u) {
-      const int run = lane + 64 * u;
-      quantize_run(hr, run, run < 16 * KBD, s_hq, s_he);
-    }
+    for (int u = 0; u < NU; ++u)
+      quantize_loaded(v[u], lane + 64 * u, lane + 64 * u < 16 * KBD, s_hq, s_he);
     wave_lds_sync();
     float acc[RG];
 #pragma unroll

@@ -179,11 +179,12 @@ __device__ inline float group_sum_last(float v) {
   return v;
 }
 
-// Order-preserving map of a float32 to uint32 (larger float -> larger key);
-// -0 is first folded to +0 so the two compare equal.
+// Order-preserving map of a float32 to uint32 (larger float -> larger key):
+// negative floats have all bits flipped, others only the sign bit.  Adding
+// +0 first turns -0 into +0 (round to nearest), so the two compare equal.
 __device__ inline uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
 }
 
 // Inverse of float_key (a -0 comes back as +0).

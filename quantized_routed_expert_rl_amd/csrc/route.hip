@@ -83,14 +83,14 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int layer, int n_slots,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
     uint32_t* miss_count, uint32_t* early_out) {
-  __shared__ __align__(16) uint32_t s_key[64 * N];
-  __shared__ __align__(16) int s_idx[64 * N];
+  __shared__ __align__(16) TopkLds s_tk;
   __shared__ int sel_ids[32];
   __shared__ float sel_lg[32];
+  __shared__ int sel_res[32];
   const int t = blockIdx.x;
-  wave_topk<N>(logits + int64_t(t) * E, E, k, s_key, s_idx, sel_ids, sel_lg);
-  const int miss = finish_token(sel_ids, sel_lg, k, E, n_slots,
-                                residency + int64_t(layer) * E, ids + int64_t(t) * k,
+  wave_topk<N>(logits + int64_t(t) * E, E, k, residency + int64_t(layer) * E, s_tk, sel_ids,
+               sel_lg, sel_res);
+  const int miss = finish_token(sel_ids, sel_lg, sel_res, k, E, n_slots, ids + int64_t(t) * k,
                                 weights + int64_t(t) * k, slots + int64_t(t) * k);
   if ((threadIdx.x & 63) == 0 && miss > 0) {
     atomicAdd(miss_count, uint32_t(miss));
