@@ -69,11 +69,13 @@ class DeviceModel:
         self.residency = to_dev(self.table.astype(np.int32))
         if pool is None:
             pool = torch.empty(max(n_slots, 1), self.slot_bytes, dtype=torch.uint8, device=DEV)
-            step = 256
+            step = min(512, max(n_slots, 1))
+            stage = torch.empty(step, self.slot_bytes, dtype=torch.uint8, pin_memory=True)
             for s0 in range(0, n_slots, step):
                 cnt = min(step, n_slots - s0)
-                pool[s0:s0 + cnt].copy_(torch.from_numpy(
-                    synth.fill_slots(w, self.table, s0, cnt, seed)))
+                synth.fill_slots(w, self.table, s0, cnt, seed, out=stage.numpy())
+                pool[s0:s0 + cnt].copy_(stage[:cnt])
+            del stage
         self.pool = pool
         self.seed = seed
 

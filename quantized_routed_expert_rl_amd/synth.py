@@ -71,25 +71,42 @@ def slot_nbytes(hidden: int, width: int, qbits: int) -> int:
     return 3 * tensor_nbytes(hidden * width, qbits)
 
 
+def _random_bytes(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n uniform random bytes (whole 64-bit draws, the fastest numpy path)."""
+    words = rng.integers(0, 2**64 - 1, (n + 7) // 8, dtype=np.uint64, endpoint=True)
+    return words.view(np.uint8)[:n]
+
+
 def random_tensor(rng: np.random.Generator, n_elems: int, qbits: int,
-                  d_low: float = 0.01, d_high: float = 0.05) -> np.ndarray:
+                  d_low: float = 0.01, d_high: float = 0.05, out: np.ndarray = None) -> np.ndarray:
+    """One block-format tensor of random codes and group scales, with block
+    scales d ~ U(d_low, d_high) rounded to float16; written into ``out``
+    (tensor_nbytes long) when given.  Padding between planes is zero."""
     lay = plane_offsets(n_elems, qbits)
     nb = lay["nb"]
-    buf = np.zeros(lay["total"], np.uint8)
-    buf[lay["q"]:lay["q"] + nb * 64] = np.frombuffer(rng.bytes(nb * 64), np.uint8)
+    buf = np.zeros(lay["total"], np.uint8) if out is None else out
+    if out is not None:
+        buf[:] = 0
+    buf[lay["q"]:lay["q"] + nb * 64] = _random_bytes(rng, nb * 64)
     if qbits == 3:
-        buf[lay["hb"]:lay["hb"] + nb * 32] = np.frombuffer(rng.bytes(nb * 32), np.uint8)
-    buf[lay["s"]:lay["s"] + nb * 4] = np.frombuffer(rng.bytes(nb * 4), np.uint8)
+        buf[lay["hb"]:lay["hb"] + nb * 32] = _random_bytes(rng, nb * 32)
+    buf[lay["s"]:lay["s"] + nb * 4] = _random_bytes(rng, nb * 4)
     d = rng.uniform(d_low, d_high, nb).astype(np.float16)
     buf[lay["d"]:lay["d"] + nb * 2] = d.view(np.uint8)
     return buf
 
 
-def expert_slot(w: Workload, layer: int, expert: int, seed: int = 0) -> np.ndarray:
-    """Bytes of one expert slot (gate, up, down) of ``layer``/``expert``."""
+def expert_slot(w: Workload, layer: int, expert: int, seed: int = 0,
+                out: np.ndarray = None) -> np.ndarray:
+    """Bytes of one expert slot (gate, up, down) of ``layer``/``expert``,
+    written into ``out`` (slot_nbytes long) when given."""
     rng = _rng(seed, w.wid, K_EXPERT, layer, expert)
     n = w.hidden * w.width
-    return np.concatenate([random_tensor(rng, n, w.qbits) for _ in range(3)])
+    tb = tensor_nbytes(n, w.qbits)
+    buf = np.empty(3 * tb, np.uint8) if out is None else out
+    for i in range(3):
+        random_tensor(rng, n, w.qbits, out=buf[i * tb:(i + 1) * tb])
+    return buf
 
 
 def router_weights(w: Workload, layer: int, seed: int = 0) -> np.ndarray:
@@ -155,13 +172,19 @@ def build_pool(w: Workload, table: np.ndarray, seed: int = 0) -> np.ndarray:
 
 
 def fill_slots(w: Workload, table: np.ndarray, start: int, count: int,
-               seed: int = 0) -> np.ndarray:
-    """Bytes of slots [start, start+count) as a [count x slot_bytes] array."""
+               seed: int = 0, out: np.ndarray = None) -> np.ndarray:
+    """Bytes of slots [start, start+count) as a [count x slot_bytes] array,
+    written into ``out`` (at least count rows) when given: reusing one
+    buffer keeps page faults out of large pools."""
     sb = slot_nbytes(w.hidden, w.width, w.qbits)
-    out = np.zeros((count, sb), np.uint8)
-    inv = {int(s): (l, e) for (l, e), s in np.ndenumerate(table) if s >= 0}
-    for i in range(count):
-        le = inv.get(start + i)
-        if le is not None:
-            out[i] = expert_slot(w, le[0], le[1], seed)
+    if out is None:
+        out = np.zeros((count, sb), np.uint8)
+    else:
+        out = out[:count]
+        out[:] = 0
+    flat = table.ravel()
+    E = table.shape[1]
+    held = np.nonzero((flat >= start) & (flat < start + count))[0]
+    for i in held:
+        expert_slot(w, int(i) // E, int(i) % E, seed, out=out[int(flat[i]) - start])
     return out
