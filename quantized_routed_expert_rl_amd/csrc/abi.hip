@@ -154,7 +154,7 @@ DecodeArgs decode_args(const rl_moe_desc* d, int32_t layer, const float* x, cons
   da.early_out = route->early_out;
   da.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   da.y = y;
-  da.mfma = d->qbits == 2 && d->width % 256 == 0;
+  da.mfma = d->width % 256 == 0;
   return da;
 }
 
@@ -198,7 +198,7 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
   a.xe = i32(l.xe);
   a.hq = s + l.hq;
   a.he = i32(l.he);
-  a.mfma = d->qbits == 2 && d->width % 256 == 0;
+  a.mfma = d->width % 256 == 0;
   a.tile_tokens = a.mfma ? 12 : 8;
   a.y = y;
   return a;

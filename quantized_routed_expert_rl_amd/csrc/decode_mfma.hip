@@ -1,6 +1,6 @@
 // Single-token decode expert GEMVs on the int8 matrix cores of gfx950, for
-// the 2-bit block format when the expert width is a multiple of 256 (the
-// operands are described in rl_mfma.h).  Same three-kernel structure and
+// 2-bit and 3-bit block weights when the expert width is a multiple of 256
+// (the operands are described in rl_mfma.h).  Same three-kernel structure and
 // routing rules as decode.hip ("Red Lite dev21 - GPU-routed decode", "What
 // changed"; "Red Lite dev23", "What changed": with the flag set every expert
 // kernel returns at once; "Red Lite dev20", "What changed": a token's experts
@@ -47,7 +47,7 @@ __device__ inline void load_b_diag(const uint8_t* xq, int h, int lane, v4i B[4])
 // float, into acc[il] (output row 4*(lane/16)/BPT + il of the tile).
 // dh: the lane's block scale bits from its A tile; xe: exponents of the
 // vector's K-blocks.
-template <int BPT>
+template <int BPT, int QBITS>
 __device__ inline void diag_accumulate(const v4i& D, uint32_t dh, const int* xe, int h, int lane,
                                        float* acc) {
   constexpr int RG = 4 / BPT;
@@ -59,7 +59,7 @@ __device__ inline void diag_accumulate(const v4i& D, uint32_t dh, const int* xe,
   for (int il = 0; il < RG; ++il) {
     const int v = BPT * il + b;
     // block scale of A row 4g + v, held by A lane 4g + v (quad 0)
-    const float dq = dh_dq(uint32_t(__shfl(int(dh), 4 * g + v, kWave)));
+    const float dq = dh_dq<QBITS>(uint32_t(__shfl(int(dh), 4 * g + v, kWave)));
     const float t = float(sel4(D, v)) * ldexpf(dq, sh);
     acc[il] += useful ? t : 0.f;
   }
@@ -125,7 +125,7 @@ __device__ __forceinline__ void quantize_loaded(const float* v, int run, bool ac
 // renormalised weights and writes ids, weights, slots, the miss count and
 // the flag; a work block only needs its slots.  Work block = (rank r, 4*RPT rows j); wave w takes
 // RPT rows of gate and up over all KB = H/256 K-blocks: 2*NH diagonal tiles.
-template <int N, int KB>
+template <int N, int KB, int QBITS>
 __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
     const float* __restrict__ x, const float* __restrict__ logits,
@@ -180,22 +180,20 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
   TileCodes cg[NH], cu[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    cg[h] = load_tile(tg, pv, blk + BPT * h, q);
-    cu[h] = load_tile(tu, pv, blk + BPT * h, q);
+    cg[h] = load_tile<QBITS>(tg, pv, blk + BPT * h, q);
+    cu[h] = load_tile<QBITS>(tu, pv, blk + BPT * h, q);
   }
   float ag[RG], au[RG];
 #pragma unroll
   for (int il = 0; il < RG; ++il) ag[il] = au[il] = 0.f;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    v4i B[4], A[4];
+    v4i B[4];
     load_b_diag<BPT>(s_xq, h, lane, B);
-    dequant_tile(cg[h], A);
-    const v4i Dg = mfma4(A, B);
-    dequant_tile(cu[h], A);
-    const v4i Du = mfma4(A, B);
-    diag_accumulate<BPT>(Dg, cg[h].dh, s_xe, h, lane, ag);
-    diag_accumulate<BPT>(Du, cu[h].dh, s_xe, h, lane, au);
+    const v4i Dg = tile_mfma<QBITS>(cg[h], B);
+    const v4i Du = tile_mfma<QBITS>(cu[h], B);
+    diag_accumulate<BPT, QBITS>(Dg, cg[h].dh, s_xe, h, lane, ag);
+    diag_accumulate<BPT, QBITS>(Du, cu[h].dh, s_xe, h, lane, au);
   }
 #pragma unroll
   for (int il = 0; il < RG; ++il) {
@@ -216,7 +214,7 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
 // in its own LDS region while its down codes load, runs NH diagonal tiles,
 // and leaves e_r[i] in LDS; then y[i] = fma(w_r, e_r[i], acc), r = 0..k-1.
 // Dynamic LDS: nw * (KBD*1024 + KBD*4) + k*RPT*4 bytes.
-template <int KBD>
+template <int KBD, int QBITS>
 __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
     PoolView pv, int H, int F, int k, const int32_t* __restrict__ slots,
     const float* __restrict__ weights, const float* __restrict__ hbuf,
@@ -251,7 +249,7 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
     const uint8_t* td = tensor_base(pv, slot, 2);
     TileCodes cd[NH];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) cd[h] = load_tile(td, pv, blk + BPT * h, q);
+    for (int h = 0; h < NH; ++h) cd[h] = load_tile<QBITS>(td, pv, blk + BPT * h, q);
 #pragma unroll
     for (int u = 0; u < NU; ++u)
       quantize_loaded(v[u], lane + 64 * u, lane + 64 * u < 16 * KBD, s_hq, s_he);
@@ -261,11 +259,10 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
     for (int il = 0; il < RG; ++il) acc[il] = 0.f;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      v4i B[4], A[4];
+      v4i B[4];
       load_b_diag<BPT>(s_hq, h, lane, B);
-      dequant_tile(cd[h], A);
-      const v4i D = mfma4(A, B);
-      diag_accumulate<BPT>(D, cd[h].dh, s_he, h, lane, acc);
+      const v4i D = tile_mfma<QBITS>(cd[h], B);
+      diag_accumulate<BPT, QBITS>(D, cd[h].dh, s_he, h, lane, acc);
     }
 #pragma unroll
     for (int il = 0; il < RG; ++il) acc[il] = group_sum_last<16>(acc[il]);
@@ -285,23 +282,28 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
 }
 
 // ------------------------------------------------------------ launchers
-template <int N, int KB>
+template <int N, int KB, int QBITS>
 static void gateup_mfma(const DecodeArgs& a, hipStream_t st) {
   constexpr int BPT = KB < 4 ? KB : 4;
   const int blocks = a.k * (a.F / (4 * (16 / BPT))) + 1;
-  decode_topk_gateup_mfma_kernel<N, KB><<<blocks, 256, 0, st>>>(
+  decode_topk_gateup_mfma_kernel<N, KB, QBITS><<<blocks, 256, 0, st>>>(
       a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
       a.weights, a.slots, a.miss_count, a.early_out, a.hbuf);
 }
 
+template <int N, int QBITS>
+static void gateup_mfma_h(const DecodeArgs& a, hipStream_t st) {
+  switch (a.H / 256) {
+    case 1: gateup_mfma<N, 1, QBITS>(a, st); break;
+    case 2: gateup_mfma<N, 2, QBITS>(a, st); break;
+    case 4: gateup_mfma<N, 4, QBITS>(a, st); break;
+    default: gateup_mfma<N, 8, QBITS>(a, st); break;
+  }
+}
+
 template <int N>
 static void gateup_mfma_n(const DecodeArgs& a, hipStream_t st) {
-  switch (a.H / 256) {
-    case 1: gateup_mfma<N, 1>(a, st); break;
-    case 2: gateup_mfma<N, 2>(a, st); break;
-    case 4: gateup_mfma<N, 4>(a, st); break;
-    default: gateup_mfma<N, 8>(a, st); break;
-  }
+  if (a.qbits == 3) gateup_mfma_h<N, 3>(a, st); else gateup_mfma_h<N, 2>(a, st);
 }
 
 void launch_decode_gateup_mfma(const DecodeArgs& a, hipStream_t st) {
@@ -323,22 +325,22 @@ int decode_down_mfma_waves(int k, int F) {
   return nw < cap ? nw : cap;
 }
 
-template <int KBD>
+template <int KBD, int QBITS>
 static void down_mfma(const DecodeArgs& a, hipStream_t st) {
   constexpr int BPT = KBD < 4 ? KBD : 4;
   constexpr int RPT = 16 / BPT;
   const int nw = decode_down_mfma_waves(a.k, a.F);
   const size_t lds = size_t(nw) * (KBD * 1024 + KBD * 4) + size_t(a.k) * RPT * 4;
-  decode_down_sum_mfma_kernel<KBD><<<a.H / RPT, 64 * nw, lds, st>>>(
+  decode_down_sum_mfma_kernel<KBD, QBITS><<<a.H / RPT, 64 * nw, lds, st>>>(
       a.pool, a.H, a.F, a.k, a.slots, a.weights, a.hbuf, a.early_out, a.y);
 }
 
 void launch_decode_down_sum_mfma(const DecodeArgs& a, hipStream_t st) {
   switch (a.F / 256) {
-    case 1: down_mfma<1>(a, st); break;
-    case 2: down_mfma<2>(a, st); break;
-    case 4: down_mfma<4>(a, st); break;
-    default: down_mfma<8>(a, st); break;
+    case 1: a.qbits == 3 ? down_mfma<1, 3>(a, st) : down_mfma<1, 2>(a, st); break;
+    case 2: a.qbits == 3 ? down_mfma<2, 3>(a, st) : down_mfma<2, 2>(a, st); break;
+    case 4: a.qbits == 3 ? down_mfma<4, 3>(a, st) : down_mfma<4, 2>(a, st); break;
+    default: a.qbits == 3 ? down_mfma<8, 3>(a, st) : down_mfma<8, 2>(a, st); break;
   }
 }
 

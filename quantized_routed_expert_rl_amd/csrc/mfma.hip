@@ -1,6 +1,6 @@
 // Batched expert projections on the int8 matrix cores of gfx950
-// (v_mfma_i32_16x16x64_i8), for the 2-bit block format when both expert
-// dimensions are multiples of 256 ("Red Lite dev20 - batched prompt
+// (v_mfma_i32_16x16x64_i8), for 2-bit and 3-bit block weights when both
+// expert dimensions are multiples of 256 ("Red Lite dev20 - batched prompt
 // ingestion", "What changed": batched gate/up and down over (expert, token)
 // pairs sorted by expert).
 //
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
 // independent MFMA chains per row tile, issued interleaved.
 constexpr int kProjWaves = 8;
 
-template <bool GATEUP>
+template <bool GATEUP, int QBITS>
 __global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
     PoolView pv, int H, int F, int k, const uint8_t* __restrict__ aq,
     const int32_t* __restrict__ ae, const uint32_t* __restrict__ early_out,
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
     TileCodes ta0, ta1, tb0, tb1;        // double-buffered codes of the two tiles
     cr0 = *reinterpret_cast<const uint4*>(src0);
     cr1 = *reinterpret_cast<const uint4*>(src1);
-    ta0 = load_tile(t0p, pv, blk0, q);
-    ta1 = load_tile(t1p, pv, blk1, q);
+    ta0 = load_tile<QBITS>(t0p, pv, blk0, q);
+    ta1 = load_tile<QBITS>(t1p, pv, blk1, q);
     *reinterpret_cast<uint4*>(&s_b[0][c0 * 16]) =
         make_uint4(cr0.x & m0, cr0.y & m0, cr0.z & m0, cr0.w & m0);
     if (c1 < 768)
@@ -153,22 +153,26 @@ __global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
       if (more) {
         cr0 = *reinterpret_cast<const uint4*>(src0 + (kb + 1) * 1024);
         cr1 = *reinterpret_cast<const uint4*>(src1 + (kb + 1) * 1024);
-        tb0 = load_tile(t0p, pv, blk0 + kb + 1, q);
-        tb1 = load_tile(t1p, pv, blk1 + kb + 1, q);
+        tb0 = load_tile<QBITS>(t0p, pv, blk0 + kb + 1, q);
+        tb1 = load_tile<QBITS>(t1p, pv, blk1 + kb + 1, q);
       }
       // d/32 of output rows 4q+v of both tiles, through LDS
       if (q == 0) {
-        s_rs[w][0][row] = tile_dq(ta0);
-        s_rs[w][1][row] = tile_dq(ta1);
+        s_rs[w][0][row] = tile_dq<QBITS>(ta0);
+        s_rs[w][1][row] = tile_dq<QBITS>(ta1);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const float4 ds0 = *reinterpret_cast<const float4*>(&s_rs[w][0][4 * q]);
       const float4 ds1 = *reinterpret_cast<const float4*>(&s_rs[w][1][4 * q]);
-      v4i A0[4], A1[4];
+      v4i A0[4], A1[4], G0[4], G1[4];
       dequant_tile(ta0, A0);
       dequant_tile(ta1, A1);
+      if (QBITS == 3) {                  // third-bit operands
+        dequant_tile_hi(ta0, G0);
+        dequant_tile_hi(ta1, G1);
+      }
       v4i D0[3], D1[3];
 #pragma unroll
       for (int ct = 0; ct < 3; ++ct) {
@@ -190,6 +194,14 @@ __global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
 #pragma unroll
         for (int ct = 0; ct < 3; ++ct)
           D1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[m], Bm[ct], D1[ct], 0, 0, 0);
+        if (QBITS == 3) {
+#pragma unroll
+          for (int ct = 0; ct < 3; ++ct)
+            D0[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(G0[m], Bm[ct], D0[ct], 0, 0, 0);
+#pragma unroll
+          for (int ct = 0; ct < 3; ++ct)
+            D1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(G1[m], Bm[ct], D1[ct], 0, 0, 0);
+        }
       }
       float f[3] = {1.f, 1.f, 1.f};
       if (!GATEUP) {
@@ -271,14 +283,16 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
 
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  prefill_proj_mfma_kernel<true><<<512, 512, 0, st>>>(
+  auto kern = a.qbits == 3 ? prefill_proj_mfma_kernel<true, 3> : prefill_proj_mfma_kernel<true, 2>;
+  kern<<<512, 512, 0, st>>>(
       a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
       p.bucket_start, p.bucket_slot, p.pairs, a.hbuf);
 }
 
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  prefill_proj_mfma_kernel<false><<<512, 512, 0, st>>>(
+  auto kern = a.qbits == 3 ? prefill_proj_mfma_kernel<false, 3> : prefill_proj_mfma_kernel<false, 2>;
+  kern<<<512, 512, 0, st>>>(
       a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
       p.bucket_start, p.bucket_slot, p.pairs, a.ebuf);
 }

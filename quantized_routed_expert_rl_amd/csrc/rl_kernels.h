@@ -40,7 +40,7 @@ struct DecodeArgs {
   uint32_t* early_out;
   float* hbuf;          // [k][F] scratch
   float* y;
-  bool mfma;            // int8 matrix-core expert kernels (2-bit, F % 256 == 0)
+  bool mfma;            // int8 matrix-core expert kernels (F % 256 == 0)
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);
@@ -76,7 +76,7 @@ struct PrefillArgs {
   const float* weights;
   const uint32_t* early_out;
   PlanPtrs plan;
-  bool mfma;        // int8 matrix-core path (2-bit, F % 256 == 0)
+  bool mfma;        // int8 matrix-core path (F % 256 == 0)
   int tile_tokens;  // tokens per token tile of a bucket
   float* hbuf;      // [T*k][F], rows in sorted pair order
   float* ebuf;      // [T*k][H], rows by pair id p = t*k + r

@@ -25,6 +25,11 @@ def real():
     return _model("decode_1l")
 
 
+@pytest.fixture(scope="module")
+def real3():
+    return _model("decode_1l", 3)
+
+
 def _decode_tokens(model, xs, layer=0):
     w = model.w
     scratch = model.decode_scratch()
@@ -79,6 +84,22 @@ def test_decode_real_shape_sampled(real):
         _, y_ref, _ = O.decode_layer(shape_of(w), x[t], real.router[0].cpu().numpy(), None,
                                      real.table[0], real.read_slot)
         close(ys[t].cpu().numpy(), y_ref, f"y token {t}")
+
+
+def test_decode_real_shape_3bit_sampled(real3):
+    """The same layer with 3-bit block weights (third code bit in its own
+    plane): ids and slots of 24 tokens exact, y of 4 against the oracle."""
+    w = real3.w
+    x = synth.activations(w, 24, stream=8)
+    outs, ys = _decode_tokens(real3, x)
+    ref = oracle_route(real3, 0, x)
+    for t in range(24):
+        assert np.array_equal(outs[t].ids.cpu().numpy()[0], ref.ids[t]), t
+        assert np.array_equal(outs[t].slots.cpu().numpy()[0], ref.slots[t]), t
+    for t in (0, 5, 13, 23):
+        _, y_ref, _ = O.decode_layer(shape_of(w), x[t], real3.router[0].cpu().numpy(), None,
+                                     real3.table[0], real3.read_slot)
+        close(ys[t].cpu().numpy(), y_ref, f"y token {t} (3-bit)")
 
 
 def test_decode_early_out_leaves_y(real):

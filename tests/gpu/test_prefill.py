@@ -86,6 +86,23 @@ def test_prefill_real_chunk_sampled(real):
     assert not np.isnan(yg).any()
 
 
+def test_prefill_real_chunk_3bit_sampled():
+    """A 512-token chunk with 3-bit block weights: routing and plan exact, y of
+    6 sampled tokens against the oracle."""
+    m3 = DeviceModel(workloads.get("prefill_1l", 3))
+    w = m3.w
+    x = synth.activations(w, 512, stream=5)
+    out, y, scratch = run_chunk(m3, x, 512)
+    sample = [0, 3, 200, 256, 480, 511]
+    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, m3.router[0].cpu().numpy(), None,
+                                     m3.table[0], m3.read_slot, 512, tokens=sample)
+    check_route(out, r)
+    check_plan(m3, scratch, 512, plan, 512, w.top_k)
+    yg = y.cpu().numpy()
+    close(yg[sample], y_ref[sample], "y sample (3-bit)")
+    assert not np.isnan(yg).any()
+
+
 def test_prefill_plan_cap_and_chunk_invariance(real):
     """y does not depend on the plan cap nor on how the prompt is chunked."""
     w = real.w
