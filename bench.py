@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
+    ap.add_argument("--stacks", action="store_true",
+                    help="also time the 48-layer stacks (decode_48l, prefill_48l 2-bit and 3-bit)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -270,8 +272,8 @@ def main():
                        "chunk_frac_of_hbm": round(chunk_bytes / (p_ms * 1e-3) / 1e9
                                                   / PEAK_HBM_GBS, 4)},
             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-            "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_proj_mfma_kernel<true>",
-                                    "down": "quantize_rows_kernel<false> + prefill_proj_mfma_kernel<false>"
+            "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_expert32_kernel<true, 2>",
+                                    "down": "quantize_rows_kernel<true> + prefill_expert32_kernel<false, 2>"
                                     }[dom] if w3.qbits == 2 and w3.width % 256 == 0 else f"prefill {dom} stage",
                          "bound": "hbm",
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -279,6 +281,59 @@ def main():
                          "traffic": stored_traffic("prefill_" + dom),
                          "bytes_per_launch": gb[dom]},
         }
+
+    # ------------------------------------------------------------ stacks
+    if args.stacks:
+        from quantized_routed_expert_rl_amd.stack import DecodeStack, PrefillStack
+        stacks = {}
+        wd = workloads.get("decode_48l")
+        md = DeviceModel(wd)
+        ds = DecodeStack(md)
+        Xd = to_dev(synth.activations(wd, wd.tokens))
+        xin = torch.empty(wd.hidden, device="cuda")
+        with torch.cuda.stream(stream):
+            xin.copy_(Xd[0])
+            ds.token(xin)
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd, stream=stream):
+                ds.token(xin)
+            stream.synchronize()
+            t0 = time.perf_counter()
+            for t in range(wd.tokens):
+                xin.copy_(Xd[t])
+                gd.replay()
+            stream.synchronize()
+            dt = time.perf_counter() - t0
+        flags = torch.stack([r.early_out for r in ds.routes]).cpu().numpy().ravel()
+        stacks["decode_48l"] = {
+            "tokens_per_s": round(wd.tokens / dt, 1), "us_per_token": round(dt * 1e6 / wd.tokens, 2),
+            "layers": wd.n_layers, "flagged_layers_last_token": int(flags.sum()),
+            "workload": "256 sequential tokens through 48 decode layers, Zipf-biased routing, "
+                        "4608 of 24576 experts resident; one HIP graph per token"}
+        del md, ds
+        torch.cuda.empty_cache()
+        for qb in (2, 3):
+            wp = workloads.get("prefill_48l", qb)
+            mp_ = DeviceModel(wp)
+            ps = PrefillStack(mp_, wp.chunks, wp.plan_cap)
+            Xp = to_dev(synth.activations(wp, wp.tokens))
+            with torch.cuda.stream(stream):
+                ps.prompt(Xp)
+                stream.synchronize()
+                reps = 3
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    ps.prompt(Xp)
+                stream.synchronize()
+                dt = (time.perf_counter() - t0) / reps
+            stacks[f"prefill_48l_{qb}bit"] = {
+                "prompt_tokens_per_s": round(wp.tokens / dt, 1), "ms_per_prompt": round(dt * 1e3, 3),
+                "token_layers_per_s": round(wp.tokens * wp.n_layers / dt, 1),
+                "workload": f"1100-token prompt in chunks 512/512/76 through 48 prefill layers, "
+                            f"Zipf-biased routing, all experts resident, {qb}-bit block weights"}
+            del mp_, ps
+            torch.cuda.empty_cache()
+        line["stacks"] = stacks
 
     # -------------------------------------------------------- cpu oracle
     if not args.no_cpu_baseline:

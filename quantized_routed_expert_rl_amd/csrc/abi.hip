@@ -199,7 +199,7 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
   a.hq = s + l.hq;
   a.he = i32(l.he);
   a.mfma = d->width % 256 == 0;
-  a.tile_tokens = a.mfma ? 12 : 8;
+  a.tile_tokens = a.mfma ? 16 : 8;   // tokens per matrix-core pass / VALU tile
   a.y = y;
   return a;
 }

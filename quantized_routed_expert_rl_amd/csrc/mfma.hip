@@ -12,7 +12,11 @@
 
 namespace rl {
 
-constexpr int kMT = 12;   // tokens per token tile: 3 column tiles of 4 tokens x 4 digits
+__device__ inline void wave_lds_sync32() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // --------------------------------------------------------------- digits
 // Rows of K float32 values -> operand-ready digit bytes.  Row r goes to
@@ -68,199 +72,260 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   if ((k0 & 255) == 0) ex[int64_t(r) * (K >> 8) + kb] = e;
 }
 
-// -------------------------------------------------- batched projections
-// One kernel for both projections.  Work item = (token tile of <= 12 tokens
-// of one bucket, 128 rows j of gate and up) or (token tile, 256 rows i of
-// down).  Block = 8 waves over the same token tile; wave w owns two 16-row
-// tiles: gate and up of rows j0+16w (gate/up), or rows i0+32w and i0+32w+16
-// (down).  K runs over 256-value blocks: the tile's digit operands for block
-// kb+1 are copied to LDS (double buffer) and the wave's codes for kb+1 are
-// loaded while block kb computes.  The three 4-token column tiles give three
-// independent MFMA chains per row tile, issued interleaved.
-constexpr int kProjWaves = 8;
+// ------------------------------------ batched projections, 32x32 tiles
+// v_mfma_i32_32x32x32_i8 (checked on the device): A lane l holds row l%32
+// and 16 bytes of K-half l/32, B lane l column l%32 and the same K-half,
+// pairing byte for byte; output lane l, v is row 8(v/4) + 4(l/32) + v%4,
+// column l%32.  A 256-value block takes 8 MFMAs; MFMA n pairs the 16-value
+// runs n (half 0) and 8 + n (half 1), so a lane's codes for a block are 32
+// contiguous bytes of its row.  Columns are 4 * token + digit: 8 tokens per
+// column tile, kCT column tiles per pass, so each dequantised weight serves
+// 8 * kCT tokens.
+//
+// One 32-row tile per wave.  Gate/up: rows 0-15 are gate rows j0 .. j0+15
+// and rows 16-31 the up rows of the same j, so output registers v and v + 8
+// of a lane hold gate and up of one (j, token) and SwiGLU stays in the lane.
+// Work item = (bucket, pass of 8 * kCT of its tokens) over all rows: 8 waves
+// share the pass's operands and each sweeps every eighth 32-row tile.  The
+// item first copies its tokens' digit operands for every K-block from
+// memory straight into LDS (global_load_lds, no registers), then runs
+// without a block barrier while each wave keeps a ring of its next code
+// blocks in flight across tile boundaries.
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kCT = 2;             // column tiles per pass
+constexpr int kPassTok = 8 * kCT;  // tokens per pass
+constexpr int kTokStride = 1040;   // LDS bytes per staged token: 1024 + 16 spreads the banks
+
+struct RowCodes {                  // one lane's share of a row's 256-value block
+  uint4 lo, hi;                    // runs 8h .. 8h+7 (16 codes, 4 bytes each)
+  uint32_t s;                      // group scales of groups 4h .. 4h+3 (16 bits)
+  uint32_t dh;                     // block scale d (binary16 bits)
+  uint4 hb;                        // third code bit of the 128 codes (3-bit only)
+};
+
+template <int QBITS>
+__device__ inline RowCodes load_row_codes(const uint8_t* t, const PoolView& p, int64_t blk,
+                                          int h) {
+  RowCodes r;
+  r.lo = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h);
+  r.hi = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h + 16);
+  r.s = *reinterpret_cast<const uint16_t*>(t + p.s + 4 * blk + 2 * h);
+  r.dh = *reinterpret_cast<const uint16_t*>(t + p.d + 2 * blk);
+  r.hb = make_uint4(0u, 0u, 0u, 0u);
+  if (QBITS == 3) r.hb = *reinterpret_cast<const uint4*>(t + p.hb + 32 * blk + 16 * h);
+  return r;
+}
+
+template <int QP>
+__device__ inline float quad_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), QP, 0xf, 0xf, false));
+}
+
+__device__ inline uint32_t sel_u4(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Byte tables of the lane's four groups 4h .. 4h+3 (MFMA n uses n/2).
+template <int QBITS>
+struct RowLuts {
+  uint32_t lo[4], hi[4];
+};
+
+template <int QBITS>
+__device__ inline RowLuts<QBITS> row_luts(const RowCodes& rc) {
+  RowLuts<QBITS> t;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t sg = (rc.s >> (4 * g)) & 15u;
+    t.lo[g] = lut2(sg);
+    t.hi[g] = QBITS == 3 ? lut_hi(sg) : 0u;
+  }
+  return t;
+}
+
+// A operand of MFMA n (run 8h + n of the lane's row): the low-bit integers,
+// and for 3-bit codes the third-bit integers in G.
+template <int QBITS>
+__device__ inline void row_operand(const RowCodes& rc, const RowLuts<QBITS>& t, int n, v4i& A,
+                                   v4i& G) {
+  A = dequant_dword(n < 4 ? sel_u4(rc.lo, n) : sel_u4(rc.hi, n - 4), t.lo[n >> 1]);
+  if (QBITS == 3) {
+    const uint32_t bits = (sel_u4(rc.hb, n >> 1) >> (16 * (n & 1))) & 0xffffu;
+    G = dequant_hi16(bits, t.hi[n >> 1]);
+  }
+}
 
 template <bool GATEUP, int QBITS>
-__global__ __launch_bounds__(512) void prefill_proj_mfma_kernel(
+__global__ __launch_bounds__(512) void prefill_expert32_kernel(
     PoolView pv, int H, int F, int k, const uint8_t* __restrict__ aq,
     const int32_t* __restrict__ ae, const uint32_t* __restrict__ early_out,
-    const int32_t* __restrict__ n_tiles_p, const int32_t* __restrict__ tile_bucket,
+    const int32_t* __restrict__ n_items_p, const int32_t* __restrict__ tile_bucket,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ bucket_start,
     const int32_t* __restrict__ bucket_slot, const int32_t* __restrict__ pairs,
     float* __restrict__ out) {
   if (*early_out) return;
-  __shared__ __align__(16) uint8_t s_b[2][kMT * 1024];
-  __shared__ int s_row[kMT];            // operand row of each token slot
-  __shared__ __align__(16) float s_rs[kProjWaves][2][16];
+  // the pass's digit operands for every K-block: token t's block kb at
+  // t * tstride + kb * 1024, tstride = KB*1024 + 144 (= 9 mod 16 in 16-byte
+  // units, so the 16 lanes of a read hit 16 different bank groups)
+  __shared__ __align__(16) uint8_t s_b[kPassTok * (8 * 1024 + 144)];
+  __shared__ int s_src[kPassTok];     // operand row of each pass token (-1: none)
+  __shared__ int s_dst[kPassTok];     // output row
+  __shared__ int s_e[kPassTok * 8];   // exponent of (token, K-block)
+  __shared__ __align__(16) float s_rs[8][32];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int row = l & 15, q = l >> 4, tk = (l & 15) >> 2, dj = l & 3;
-  const int K = GATEUP ? H : F;          // reduction length
-  const int NR = GATEUP ? F : H;         // output rows
-  const int KB = K / 256;
-  const int rows_per_item = GATEUP ? 128 : 256;
-  const int nri = NR / rows_per_item;
-  const int ntiles = *n_tiles_p;
-  for (int item = blockIdx.x; item < ntiles * nri; item += gridDim.x) {
-    const int tile = item / nri, ri = item % nri;
-    const int b = tile_bucket[tile];
-    const int pos0 = bucket_start[b] + (tile - tile_start[b]) * kMT;
-    const int rem = bucket_start[b + 1] - pos0;
-    const int nt = rem < kMT ? rem : kMT;
+  const int K = GATEUP ? H : F;
+  const int NR = GATEUP ? F : H;
+  const int KB = K / 256, kbs = __builtin_ctz(KB);
+  const int tstride = KB * 1024 + 144;
+  const int NTI = GATEUP ? NR / 16 : NR / 32;     // 32-row tiles per item
+  const int NQ = (NTI / 8) * KB;                   // (tile, K-block) steps of a wave
+  const int h = l >> 5, lr = l & 31;               // A: row lr of the tile, K-half h
+  const int tcol = lr >> 2, dcol = l & 3;          // B/D: token and digit of column lr
+  constexpr int NPF = QBITS == 3 ? 2 : 4;          // code blocks in flight
+  const int n_items = *n_items_p;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int b = tile_bucket[item];
+    const int p0 = bucket_start[b], n = bucket_start[b + 1] - p0;
+    const int c0 = (item - tile_start[b]) * kPassTok;
+    const int nt = n - c0 < kPassTok ? n - c0 : kPassTok;
     const int slot = bucket_slot[b];
-    __syncthreads();                     // previous item done with s_b, s_row
-    if (tid < nt) s_row[tid] = GATEUP ? pairs[pos0 + tid] / k : pos0 + tid;
-    __syncthreads();
-    const uint8_t* t0p = tensor_base(pv, slot, GATEUP ? 0 : 2);
-    const uint8_t* t1p = tensor_base(pv, slot, GATEUP ? 1 : 2);
-    const int r00 = GATEUP ? ri * 128 + 16 * w : ri * 256 + 32 * w;
-    const int r01 = GATEUP ? r00 : r00 + 16;
-    const int64_t blk0 = int64_t(r00 + row) * KB, blk1 = int64_t(r01 + row) * KB;
-    bool tok_ok[3];
-    int orow[3];
-#pragma unroll
-    for (int ct = 0; ct < 3; ++ct) {
-      tok_ok[ct] = 4 * ct + tk < nt;
-      orow[ct] = s_row[tok_ok[ct] ? 4 * ct + tk : 0];
+    // the wave's A stream: step q = (tile i = q >> kbs, K-block q & (KB-1));
+    // tile i is row tile w + 8i: gate/up rows 16(w+8i) .. +15 of gate (lanes
+    // lr < 16) and of up (lr >= 16); down rows 32(w+8i) + lr
+    const uint8_t* tA = tensor_base(pv, slot, GATEUP ? (lr < 16 ? 0 : 1) : 2);
+    auto blk_of = [&](int q) {
+      const int tt = w + 8 * (q >> kbs);
+      const int row = GATEUP ? 16 * tt + (lr & 15) : 32 * tt + lr;
+      return int64_t(row) * KB + (q & (KB - 1));
+    };
+    __syncthreads();                       // the previous item is done with LDS
+    if (tid < kPassTok) {
+      const int pos = p0 + c0 + tid;
+      s_src[tid] = tid < nt ? (GATEUP ? pairs[pos] / k : pos) : -1;
+      s_dst[tid] = tid < nt ? (GATEUP ? pos : pairs[pos]) : -1;
     }
-    // operand copy: 12 slots x 1 KB = 768 chunks of 16 B; thread takes chunk
-    // tid and tid+512 (the second only for tid < 256); empty slots get zeros
-    const int c0 = tid, c1 = tid + 512;
-    const uint32_t m0 = c0 < nt * 64 ? ~0u : 0u;
-    const uint32_t m1 = (c1 < 768 && c1 < nt * 64) ? ~0u : 0u;
-    const uint8_t* src0 = aq + int64_t(s_row[m0 ? (c0 >> 6) : 0]) * K * 4 + (c0 & 63) * 16;
-    const uint8_t* src1 = aq + int64_t(s_row[m1 ? (c1 >> 6) : 0]) * K * 4 + (c1 & 63) * 16;
-    float acc[2][3][4];
+    RowCodes pf[NPF];                      // a ring of code blocks in flight
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int ct = 0; ct < 3; ++ct)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][ct][v] = 0.f;
-    uint4 cr0, cr1;
-    TileCodes ta0, ta1, tb0, tb1;        // double-buffered codes of the two tiles
-    cr0 = *reinterpret_cast<const uint4*>(src0);
-    cr1 = *reinterpret_cast<const uint4*>(src1);
-    ta0 = load_tile<QBITS>(t0p, pv, blk0, q);
-    ta1 = load_tile<QBITS>(t1p, pv, blk1, q);
-    *reinterpret_cast<uint4*>(&s_b[0][c0 * 16]) =
-        make_uint4(cr0.x & m0, cr0.y & m0, cr0.z & m0, cr0.w & m0);
-    if (c1 < 768)
-      *reinterpret_cast<uint4*>(&s_b[0][c1 * 16]) =
-          make_uint4(cr1.x & m1, cr1.y & m1, cr1.z & m1, cr1.w & m1);
+    for (int i = 0; i < NPF; ++i)
+      if (i < NQ) pf[i] = load_row_codes<QBITS>(tA, pv, blk_of(i), h);
     __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-      const int buf = kb & 1;
-      const bool more = kb + 1 < KB;
-      if (more) {
-        cr0 = *reinterpret_cast<const uint4*>(src0 + (kb + 1) * 1024);
-        cr1 = *reinterpret_cast<const uint4*>(src1 + (kb + 1) * 1024);
-        tb0 = load_tile<QBITS>(t0p, pv, blk0 + kb + 1, q);
-        tb1 = load_tile<QBITS>(t1p, pv, blk1 + kb + 1, q);
+    // operands straight from memory to LDS: wave w copies tokens
+    // kPassTok/8 * w .. +kPassTok/8 - 1, one 1 KiB K-block per instruction;
+    // absent tokens are skipped (their columns are never stored)
+    constexpr int TPW = kPassTok / 8;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = TPW * w + u;
+      const int src = __builtin_amdgcn_readfirstlane(s_src[t]);
+      if (src >= 0) {
+        const uint8_t* g = aq + int64_t(src) * KB * 1024 + 16 * l;
+        uint8_t* d = &s_b[t * tstride];
+        for (int kb = 0; kb < KB; ++kb)
+          __builtin_amdgcn_global_load_lds(g + kb * 1024, d + kb * 1024, 16, 0, 0);
       }
-      // d/32 of output rows 4q+v of both tiles, through LDS
-      if (q == 0) {
-        s_rs[w][0][row] = tile_dq<QBITS>(ta0);
-        s_rs[w][1][row] = tile_dq<QBITS>(ta1);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      const float4 ds0 = *reinterpret_cast<const float4*>(&s_rs[w][0][4 * q]);
-      const float4 ds1 = *reinterpret_cast<const float4*>(&s_rs[w][1][4 * q]);
-      v4i A0[4], A1[4], G0[4], G1[4];
-      dequant_tile(ta0, A0);
-      dequant_tile(ta1, A1);
-      if (QBITS == 3) {                  // third-bit operands
-        dequant_tile_hi(ta0, G0);
-        dequant_tile_hi(ta1, G1);
-      }
-      v4i D0[3], D1[3];
-#pragma unroll
-      for (int ct = 0; ct < 3; ++ct) {
-        D0[ct] = v4i{0, 0, 0, 0};
-        D1[ct] = v4i{0, 0, 0, 0};
-      }
-      const uint8_t* bb = &s_b[buf][tk * 1024 + q * 256 + dj * 64];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v4i Bm[3];
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct) {
-          const int4 v = *reinterpret_cast<const int4*>(bb + ct * 4096 + m * 16);
-          Bm[ct] = v4i{v.x, v.y, v.z, v.w};
-        }
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct)
-          D0[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[m], Bm[ct], D0[ct], 0, 0, 0);
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct)
-          D1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[m], Bm[ct], D1[ct], 0, 0, 0);
-        if (QBITS == 3) {
-#pragma unroll
-          for (int ct = 0; ct < 3; ++ct)
-            D0[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(G0[m], Bm[ct], D0[ct], 0, 0, 0);
-#pragma unroll
-          for (int ct = 0; ct < 3; ++ct)
-            D1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(G1[m], Bm[ct], D1[ct], 0, 0, 0);
-        }
-      }
-      float f[3] = {1.f, 1.f, 1.f};
-      if (!GATEUP) {
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct) f[ct] = ldexpf(1.f, 8 * (3 - dj) - ae[int64_t(orow[ct]) * KB + kb]);
-      }
-      const float s0[4] = {ds0.x, ds0.y, ds0.z, ds0.w}, s1[4] = {ds1.x, ds1.y, ds1.z, ds1.w};
-#pragma unroll
-      for (int ct = 0; ct < 3; ++ct)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          acc[0][ct][v] = fmaf(s0[v] * f[ct], float(D0[ct][v]), acc[0][ct][v]);
-          acc[1][ct][v] = fmaf(s1[v] * f[ct], float(D1[ct][v]), acc[1][ct][v]);
-        }
-      if (more) {
-        *reinterpret_cast<uint4*>(&s_b[buf ^ 1][c0 * 16]) =
-            make_uint4(cr0.x & m0, cr0.y & m0, cr0.z & m0, cr0.w & m0);
-        if (c1 < 768)
-          *reinterpret_cast<uint4*>(&s_b[buf ^ 1][c1 * 16]) =
-              make_uint4(cr1.x & m1, cr1.y & m1, cr1.z & m1, cr1.w & m1);
-        ta0 = tb0;
-        ta1 = tb1;
-      }
-      __syncthreads();
+      if (l < KB) s_e[t * 8 + l] = src >= 0 ? ae[int64_t(src) * KB + l] : 0;
     }
-    // combine each token's 4 digit columns; store
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float acc[kCT][16];
+    for (int q0 = 0; q0 < NQ; q0 += NPF)
 #pragma unroll
-    for (int ct = 0; ct < 3; ++ct) {
-      const int n = 4 * ct + tk;
-      if (GATEUP) {
-        const float fx = ldexpf(1.f, 8 * (3 - dj) - (tok_ok[ct] ? ae[int64_t(orow[ct]) * KB] : 0));
-        float h[4];
+    for (int ip = 0; ip < NPF; ++ip) {
+      const int q = q0 + ip;
+      if (q >= NQ) break;
+      const int kb = q & (KB - 1);
+      const RowCodes ca = pf[ip];
+      if (q + NPF < NQ) pf[ip] = load_row_codes<QBITS>(tA, pv, blk_of(q + NPF), h);
+      if (kb == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float g = acc[0][ct][v] * fx, u = acc[1][ct][v] * fx;
-          g += __shfl_xor(g, 1, kWave);
-          g += __shfl_xor(g, 2, kWave);
-          u += __shfl_xor(u, 1, kWave);
-          u += __shfl_xor(u, 2, kWave);
-          h[v] = silu_mul(g, u);
+        for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
+      }
+      if (h == 0) s_rs[w][lr] = dh_dq<QBITS>(ca.dh);   // row scales through LDS
+      wave_lds_sync32();
+      const RowLuts<QBITS> luts = row_luts<QBITS>(ca);
+      v16i D[kCT];
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) D[ct] = v16i{};
+      // B operands read one MFMA step ahead, so no MFMA waits on its own LDS
+      // read.  Chunk of run 8h + nn, digit dcol: 512h + 64dcol + 256(nn/4) +
+      // 16(nn%4) bytes into the token's K-block.
+      const uint8_t* bbase = &s_b[tcol * tstride + kb * 1024 + 512 * h + 64 * dcol];
+      auto bread = [&](int nn, int ct) {
+        const int4 v = *reinterpret_cast<const int4*>(bbase + 8 * ct * tstride +
+                                                      256 * (nn >> 2) + 16 * (nn & 3));
+        return v4i{v.x, v.y, v.z, v.w};
+      };
+      v4i Bc[2][kCT];
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) Bc[0][ct] = bread(0, ct);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) {
+        if (nn < 7) {
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) Bc[(nn + 1) & 1][ct] = bread(nn + 1, ct);
         }
-        if (dj == 0 && tok_ok[ct])
-          *reinterpret_cast<float4*>(out + int64_t(pos0 + n) * F + r00 + 4 * q) =
-              make_float4(h[0], h[1], h[2], h[3]);
-      } else {
-        const int p = tok_ok[ct] ? pairs[pos0 + n] : 0;
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's MFMAs
+        v4i A, G;
+        row_operand<QBITS>(ca, luts, nn, A, G);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float e[4];
+        for (int ct = 0; ct < kCT; ++ct) {
+          D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bc[nn & 1][ct], D[ct], 0, 0, 0);
+          if (QBITS == 3)
+            D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(G, Bc[nn & 1][ct], D[ct], 0, 0, 0);
+        }
+      }
+      // row factor d/32 (or d/64); the column factor 2^(8(3-digit) - e) is one
+      // per token (a row exponent) and applied when the tile is done
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float sv = acc[u][ct][v];
-            sv += __shfl_xor(sv, 1, kWave);
-            sv += __shfl_xor(sv, 2, kWave);
-            e[v] = sv;
+      for (int g = 0; g < 4; ++g) {
+        const float4 f = *reinterpret_cast<const float4*>(&s_rs[w][8 * g + 4 * h]);
+        const float rv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[ct][4 * g + j] = fmaf(float(D[ct][4 * g + j]), rv[j], acc[ct][4 * g + j]);
+      }
+      wave_lds_sync32();                   // row scales read before the next step's
+      if (kb == KB - 1) {
+        // tile done: combine each token's four digit columns (lanes
+        // 4*tcol .. +3) and store
+        const int tt = w + 8 * (q >> kbs);
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
+          const int dst = s_dst[8 * ct + tcol];
+          const float cs = ldexpf(1.f, 8 * (3 - dcol) - s_e[(8 * ct + tcol) * 8]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float x = acc[ct][v] * cs;
+            x += quad_swap<0xb1>(x);          // quad_perm [1,0,3,2]
+            x += quad_swap<0x4e>(x);          // quad_perm [2,3,0,1]
+            acc[ct][v] = x;
           }
-          if (dj == 0 && tok_ok[ct])
-            *reinterpret_cast<float4*>(out + int64_t(p) * H + (u ? r01 : r00) + 4 * q) =
-                make_float4(e[0], e[1], e[2], e[3]);
+          if (dcol == 0 && dst >= 0) {
+            if (GATEUP) {                  // rows R = 8g + 4h + j < 16: gate; R + 16: up
+              const int j0 = 16 * tt;
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                float4 hv;
+                hv.x = silu_mul(acc[ct][4 * g + 0], acc[ct][4 * g + 8]);
+                hv.y = silu_mul(acc[ct][4 * g + 1], acc[ct][4 * g + 9]);
+                hv.z = silu_mul(acc[ct][4 * g + 2], acc[ct][4 * g + 10]);
+                hv.w = silu_mul(acc[ct][4 * g + 3], acc[ct][4 * g + 11]);
+                *reinterpret_cast<float4*>(out + int64_t(dst) * F + j0 + 8 * g + 4 * h) = hv;
+              }
+            } else {
+              const int i0 = 32 * tt;
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(out + int64_t(dst) * H + i0 + 8 * g + 4 * h) =
+                    make_float4(acc[ct][4 * g], acc[ct][4 * g + 1], acc[ct][4 * g + 2],
+                                acc[ct][4 * g + 3]);
+            }
+          }
         }
       }
     }
@@ -277,24 +342,24 @@ void launch_quantize_x(const PrefillArgs& a, hipStream_t st) {
 void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
   const int rpb = 256 / (a.F / 16);
   const int R = a.T * a.k;
-  quantize_rows_kernel<false><<<(R + rpb - 1) / rpb, 256, 0, st>>>(a.hbuf, R, a.F, a.hq, a.he,
-                                                                    a.early_out);
+  quantize_rows_kernel<true><<<(R + rpb - 1) / rpb, 256, 0, st>>>(a.hbuf, R, a.F, a.hq, a.he,
+                                                                   a.early_out);
 }
 
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  auto kern = a.qbits == 3 ? prefill_proj_mfma_kernel<true, 3> : prefill_proj_mfma_kernel<true, 2>;
-  kern<<<512, 512, 0, st>>>(
-      a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
-      p.bucket_start, p.bucket_slot, p.pairs, a.hbuf);
+  auto kern = a.qbits == 3 ? prefill_expert32_kernel<true, 3> : prefill_expert32_kernel<true, 2>;
+  kern<<<1024, 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
+                             p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
+                             p.pairs, a.hbuf);
 }
 
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  auto kern = a.qbits == 3 ? prefill_proj_mfma_kernel<false, 3> : prefill_proj_mfma_kernel<false, 2>;
-  kern<<<512, 512, 0, st>>>(
-      a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles, p.tile_bucket, p.tile_start,
-      p.bucket_start, p.bucket_slot, p.pairs, a.ebuf);
+  auto kern = a.qbits == 3 ? prefill_expert32_kernel<false, 3> : prefill_expert32_kernel<false, 2>;
+  kern<<<1024, 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
+                             p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
+                             p.pairs, a.ebuf);
 }
 
 }  // namespace rl

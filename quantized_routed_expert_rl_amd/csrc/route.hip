@@ -18,59 +18,89 @@ namespace rl {
 // logits[t][e] = fl32(sum_i W[e][i] x[t][i] + b[e]) on the float64 matrix
 // cores (v_mfma_f64_16x16x4f64; A lane l: row l%16, K index l/16; B lane l:
 // column l%16, K index l/16; output lane l, v: row l/16 + 4v, column l%16).
-// Block = 32 tokens x 32 experts, one 16x16 tile per wave over all of K.
-// Inside each 16-value chunk c, MFMA step 4c+i of lane quad kq takes K index
-// 16c + 4kq + i for both operands, so each lane reads float4s.
+// Block = 32 tokens x 32 experts, one 16x16 tile per wave; K runs in
+// 64-value chunks staged through LDS (double buffer; the next chunk's
+// float4 loads are in flight while the current one computes), so each x and
+// W value is read from memory once per block instead of once per wave.
+// Inside each 16-value group g of a chunk, MFMA step 4g+i of lane quad kq
+// takes K index 16g + 4kq + i for both operands: one float4 LDS read per
+// lane per group.  Four accumulation chains (one per group) keep the matrix
+// core busy; summed in float64 at the end.
 typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int kRgStride = 68;   // floats per staged row: 64 + 4 keeps float4 reads conflict-free
 
 __global__ __launch_bounds__(256) void route_gemm_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
     int T, int E, int H, float* __restrict__ logits, float* __restrict__ logits_out,
     uint32_t* miss_count, uint32_t* early_out) {
-  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t0 = blockIdx.y * 32 + (wv >> 1) * 16, e0 = blockIdx.x * 32 + (wv & 1) * 16;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+  __shared__ __align__(16) float s_a[2][32 * kRgStride];   // tokens
+  __shared__ __align__(16) float s_b[2][32 * kRgStride];   // experts
+  const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+  const int tb = blockIdx.y * 32, eb = blockIdx.x * 32;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     *miss_count = 0u;
     *early_out = 0u;
   }
+  // staging: thread tid copies row tid/8, floats 8*(tid%8) .. +7 of the chunk
+  // for both operands (two float4 each)
+  const int sr = tid >> 3, sc = 8 * (tid & 7);
+  const bool va = tb + sr < T, vb = eb + sr < E;
+  const float* ga = x + int64_t(va ? tb + sr : 0) * H + sc;
+  const float* gb = W + int64_t(vb ? eb + sr : 0) * H + sc;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 pa0 = va ? *reinterpret_cast<const float4*>(ga) : z4;
+  float4 pa1 = va ? *reinterpret_cast<const float4*>(ga + 4) : z4;
+  float4 pb0 = vb ? *reinterpret_cast<const float4*>(gb) : z4;
+  float4 pb1 = vb ? *reinterpret_cast<const float4*>(gb + 4) : z4;
   const int r = l & 15, kq = l >> 4;
-  const int ta = t0 + r, eb = e0 + r;
-  const bool va = ta < T, vb = eb < E;
-  const float* xa = x + int64_t(va ? ta : 0) * H + 4 * kq;
-  const float* wb = W + int64_t(vb ? eb : 0) * H + 4 * kq;
-  // four independent accumulation chains (one per 16-value chunk of each
-  // 64-value step) keep the matrix core busy; summed in float64 at the end
+  const int ra = (wv >> 1) * 16 + r, rb = (wv & 1) * 16 + r;   // staged rows this lane reads
   v4d acc4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc4[u] = v4d{0.0, 0.0, 0.0, 0.0};
-  for (int c = 0; c < H; c += 64) {
+  const int nch = H / 64;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    *reinterpret_cast<float4*>(&s_a[buf][sr * kRgStride + sc]) = pa0;
+    *reinterpret_cast<float4*>(&s_a[buf][sr * kRgStride + sc + 4]) = pa1;
+    *reinterpret_cast<float4*>(&s_b[buf][sr * kRgStride + sc]) = pb0;
+    *reinterpret_cast<float4*>(&s_b[buf][sr * kRgStride + sc + 4]) = pb1;
+    __syncthreads();
+    if (ch + 1 < nch) {
+      const int off = (ch + 1) * 64;
+      pa0 = va ? *reinterpret_cast<const float4*>(ga + off) : z4;
+      pa1 = va ? *reinterpret_cast<const float4*>(ga + off + 4) : z4;
+      pb0 = vb ? *reinterpret_cast<const float4*>(gb + off) : z4;
+      pb1 = vb ? *reinterpret_cast<const float4*>(gb + off + 4) : z4;
+    }
     float4 av[4], bv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      av[u] = va ? *reinterpret_cast<const float4*>(xa + c + 16 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
-      bv[u] = vb ? *reinterpret_cast<const float4*>(wb + c + 16 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < 4; ++g) {
+      av[g] = *reinterpret_cast<const float4*>(&s_a[buf][ra * kRgStride + 16 * g + 4 * kq]);
+      bv[g] = *reinterpret_cast<const float4*>(&s_b[buf][rb * kRgStride + 16 * g + 4 * kq]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].x), double(bv[u].x), acc4[u], 0, 0, 0);
+    for (int g = 0; g < 4; ++g)
+      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].x), double(bv[g].x), acc4[g], 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].y), double(bv[u].y), acc4[u], 0, 0, 0);
+    for (int g = 0; g < 4; ++g)
+      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].y), double(bv[g].y), acc4[g], 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].z), double(bv[u].z), acc4[u], 0, 0, 0);
+    for (int g = 0; g < 4; ++g)
+      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].z), double(bv[g].z), acc4[g], 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc4[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[u].w), double(bv[u].w), acc4[u], 0, 0, 0);
+    for (int g = 0; g < 4; ++g)
+      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].w), double(bv[g].w), acc4[g], 0, 0, 0);
   }
   const v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  const int t0 = tb + (wv >> 1) * 16, e0 = eb + (wv & 1) * 16;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int t = t0 + kq + 4 * v, e = e0 + r;
     if (t < T && e < E) {
-      double s = acc[v];
-      if (bias) s += double(bias[e]);
-      const float lg = float(s);
+      double sum = acc[v];
+      if (bias) sum += double(bias[e]);
+      const float lg = float(sum);
       logits[int64_t(t) * E + e] = lg;
       if (logits_out) logits_out[int64_t(t) * E + e] = lg;
     }
