@@ -57,32 +57,45 @@ __global__ __launch_bounds__(64) void plan_groups_kernel(
   }
 }
 
-// One wave per expert walks the pairs of each group in order.  COUNT mode
-// stores the number of pairs of (group, expert); SCATTER mode writes each
-// matching pair id at offs[(group, expert)] + its rank among the matches
-// (so the order inside a bucket is the pair order: stable).
+// One wave per expert walks the pairs of each group in order, 16 experts per
+// block; the pairs' expert ids are staged in LDS kPairChunk at a time, so
+// each id is read from memory once per block.  COUNT mode stores the number
+// of pairs of (group, expert); SCATTER mode writes each matching pair id at
+// offs[(group, expert)] + its rank among the matches (so the order inside a
+// bucket is the pair order: stable).
+constexpr int kPairChunk = 8192;
+
 template <bool SCATTER>
-__global__ __launch_bounds__(256) void plan_pairs_kernel(
+__global__ __launch_bounds__(1024) void plan_pairs_kernel(
     const int32_t* __restrict__ ids, int k, int E, const uint32_t* __restrict__ early_out,
     const int32_t* __restrict__ n_groups, const int32_t* __restrict__ group_bounds,
     int32_t* __restrict__ counts, const int32_t* __restrict__ offs, int32_t* __restrict__ pairs) {
   if (*early_out) return;
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  __shared__ int s_ids[kPairChunk];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * 16 + wv;
+  const bool live = e < E;
   const unsigned long long below = (1ull << lane) - 1ull;
   const int ng = *n_groups;
   for (int g = 0; g < ng; ++g) {
     const int p0 = group_bounds[g] * k, p1 = group_bounds[g + 1] * k;
-    int run = SCATTER ? offs[int64_t(g) * E + e] : 0;
-    for (int base = p0; base < p1; base += 64) {
-      const int p = base + lane;
-      const bool m = p < p1 && ids[p] == e;
-      const unsigned long long mask = __ballot(m);
-      if (SCATTER && m) pairs[run + __popcll(mask & below)] = p;
-      run += __popcll(mask);
+    int run = (SCATTER && live) ? offs[int64_t(g) * E + e] : 0;
+    for (int c0 = p0; c0 < p1; c0 += kPairChunk) {
+      const int cn = p1 - c0 < kPairChunk ? p1 - c0 : kPairChunk;
+      __syncthreads();                     // the previous chunk has been scanned
+      for (int i = threadIdx.x; i < cn; i += blockDim.x) s_ids[i] = ids[c0 + i];
+      __syncthreads();
+      if (live) {
+        for (int base = 0; base < cn; base += 64) {
+          const int i = base + lane;
+          const bool m = i < cn && s_ids[i < cn ? i : 0] == e;
+          const unsigned long long mask = __ballot(m);
+          if (SCATTER && m) pairs[run + __popcll(mask & below)] = c0 + i;
+          run += __popcll(mask);
+        }
+      }
     }
-    if (!SCATTER && lane == 0) counts[int64_t(g) * E + e] = run;
+    if (!SCATTER && live && lane == 0) counts[int64_t(g) * E + e] = run;
   }
 }
 
@@ -342,14 +355,14 @@ void launch_prefill_plan(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
   plan_groups_kernel<<<1, 64, 0, st>>>(a.ids, a.T, a.k, a.E, a.plan_cap, a.early_out,
                                        p.n_groups, p.group_bounds);
-  const int blocks = (a.E + 3) / 4;
-  plan_pairs_kernel<false><<<blocks, 256, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
+  const int blocks = (a.E + 15) / 16;
+  plan_pairs_kernel<false><<<blocks, 1024, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
                                                    p.group_bounds, p.counts, nullptr, nullptr);
   plan_scan_kernel<<<1, 1024, 0, st>>>(a.E, a.layer, a.residency, a.early_out, p.n_groups,
                                        p.counts, p.offs, p.n_buckets, p.group_bucket_start,
                                        p.bucket_expert, p.bucket_start, p.bucket_slot,
                                        p.tile_start, p.n_tiles, p.tile_bucket, a.tile_tokens);
-  plan_pairs_kernel<true><<<blocks, 256, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
+  plan_pairs_kernel<true><<<blocks, 1024, 0, st>>>(a.ids, a.k, a.E, a.early_out, p.n_groups,
                                                   p.group_bounds, nullptr, p.offs, p.pairs);
 }
 
