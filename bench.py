@@ -284,8 +284,8 @@ def main():
                        "chunk_frac_of_hbm": round(chunk_bytes / (p_ms * 1e-3) / 1e9
                                                   / PEAK_HBM_GBS, 4)},
             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-            "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_expert32_kernel<true, 2>",
-                                    "down": "quantize_rows_kernel<true> + prefill_expert32_kernel<false, 2>"
+            "roofline": {"kernel": {"gateup": "quantize_rows_kernel<true> + prefill_expert_kernel<true, 2>",
+                                    "down": "quantize_rows_kernel<true> + prefill_expert_kernel<false, 2>"
                                     }[dom] if w3.qbits == 2 and w3.width % 256 == 0 else f"prefill {dom} stage",
                          "bound": "hbm",
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -78,29 +78,38 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
 // pairing byte for byte; output lane l, v is row 8(v/4) + 4(l/32) + v%4,
 // column l%32.  A 256-value block takes 8 MFMAs; MFMA n pairs the 16-value
 // runs n (half 0) and 8 + n (half 1), so a lane's codes for a block are 32
-// contiguous bytes of its row.  Columns are 4 * token + digit: 8 tokens per
-// column tile, kCT column tiles per pass, so each dequantised weight serves
-// 8 * kCT tokens.
+// contiguous bytes of one weight row.
 //
-// One 32-row tile per wave.  Gate/up: rows 0-15 are gate rows j0 .. j0+15
-// and rows 16-31 the up rows of the same j, so output registers v and v + 8
-// of a lane hold gate and up of one (j, token) and SwiGLU stays in the lane.
-// Work item = (bucket, pass of 8 * kCT of its tokens) over all rows: 8 waves
-// share the pass's operands and each sweeps every eighth 32-row tile.  The
-// item first copies its tokens' digit operands for every K-block from
-// memory straight into LDS (global_load_lds, no registers), then runs
-// without a block barrier while each wave keeps a ring of its next code
-// blocks in flight across tile boundaries.
+// A = activation digits, row 4 * token + digit (8 tokens per MFMA, kCT
+// MFMAs per pass); B = dequantised weights, column = one of a tile's 32
+// weight rows.  A lane's outputs are then its own weight row for tokens
+// 2m + l/32 (m < 4), with the four digits of each token in registers
+// 4m .. 4m+3: digits combine inside the lane, and the row's block scale d is
+// the lane's own, so scaling needs nothing from other lanes.  Gate/up tiles
+// hold gate rows j0 .. j0+15 in columns 0-15 and the up rows of the same j in
+// columns 16-31; lanes l and l^16 trade half of their tokens for SwiGLU.
+//
+// Work: item = (bucket, pass of kPassTok of its tokens) over all rows;
+// round = 8 tiles of one item, one per wave.  The rounds of all items are
+// split evenly over the blocks (one per compute unit), each taking a
+// contiguous range, so no compute unit idles while another still has whole
+// items queued.  When its range enters a new item, the block copies the
+// pass's digit operands for every K-block straight into LDS
+// (global_load_lds, no registers); in between, each wave streams its tiles'
+// codes through a ring of blocks in flight that runs across tile and item
+// boundaries.
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kCT = 2;             // column tiles per pass
+constexpr int kCT = 2;             // MFMAs (8 tokens each) per pass
 constexpr int kPassTok = 8 * kCT;  // tokens per pass
-constexpr int kTokStride = 1040;   // LDS bytes per staged token: 1024 + 16 spreads the banks
 
+// Whole dwords only: a sub-dword load is widened right after it is issued,
+// which would make the wave wait for it there and empty the ring of loads in
+// flight.  The halves are picked when the block is used.
 struct RowCodes {                  // one lane's share of a row's 256-value block
   uint4 lo, hi;                    // runs 8h .. 8h+7 (16 codes, 4 bytes each)
-  uint32_t s;                      // group scales of groups 4h .. 4h+3 (16 bits)
-  uint32_t dh;                     // block scale d (binary16 bits)
+  uint32_t s;                      // the block's eight group scales (lane uses half h)
+  uint32_t dh;                     // d of blocks 2(blk/2) and 2(blk/2)+1 (binary16 bits)
   uint4 hb;                        // third code bit of the 128 codes (3-bit only)
 };
 
@@ -110,16 +119,11 @@ __device__ inline RowCodes load_row_codes(const uint8_t* t, const PoolView& p, i
   RowCodes r;
   r.lo = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h);
   r.hi = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h + 16);
-  r.s = *reinterpret_cast<const uint16_t*>(t + p.s + 4 * blk + 2 * h);
-  r.dh = *reinterpret_cast<const uint16_t*>(t + p.d + 2 * blk);
+  r.s = *reinterpret_cast<const uint32_t*>(t + p.s + 4 * blk);
+  r.dh = *reinterpret_cast<const uint32_t*>(t + p.d + 4 * (blk >> 1));
   r.hb = make_uint4(0u, 0u, 0u, 0u);
   if (QBITS == 3) r.hb = *reinterpret_cast<const uint4*>(t + p.hb + 32 * blk + 16 * h);
   return r;
-}
-
-template <int QP>
-__device__ inline float quad_swap(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), QP, 0xf, 0xf, false));
 }
 
 __device__ inline uint32_t sel_u4(const uint4& v, int i) {
@@ -132,24 +136,44 @@ struct RowLuts {
   uint32_t lo[4], hi[4];
 };
 
+// The four tables of groups 4h .. 4h+3 at once, byte-parallel: bytes
+// m_g = 2 s_g + 1 (<= 31) and 3 m_g (<= 93) never carry, and the byte-wise
+// negation of M is 0x01010100 - M (mod 2^32) since every byte is nonzero.
+// ssel picks the lane's two scale bytes: 0x01010000 (h = 0), 0x03030202.
 template <int QBITS>
-__device__ inline RowLuts<QBITS> row_luts(const RowCodes& rc) {
+__device__ inline RowLuts<QBITS> row_luts(const RowCodes& rc, uint32_t ssel) {
   RowLuts<QBITS> t;
+  const uint32_t y = __builtin_amdgcn_perm(rc.s, rc.s, ssel);          // bytes s01 s01 s23 s23
+  const uint32_t x = (y & 0x000f000fu) | ((y >> 4) & 0x0f000f00u);    // bytes s0 s1 s2 s3
+  const uint32_t M = (x << 1) | 0x01010101u;
+  const uint32_t M3 = M + (M << 1);
+  const uint32_t nM = 0x01010100u - M, nM3 = 0x01010100u - M3;
+  const uint32_t a01 = __builtin_amdgcn_perm(nM, nM3, 0x05010400u);    // -3m0 -m0 -3m1 -m1
+  const uint32_t a23 = __builtin_amdgcn_perm(nM, nM3, 0x07030602u);
+  const uint32_t b01 = __builtin_amdgcn_perm(M3, M, 0x05010400u);      // m0 3m0 m1 3m1
+  const uint32_t b23 = __builtin_amdgcn_perm(M3, M, 0x07030602u);
+  t.lo[0] = __builtin_amdgcn_perm(b01, a01, 0x05040100u);              // -3m -m m 3m
+  t.lo[1] = __builtin_amdgcn_perm(b01, a01, 0x07060302u);
+  t.lo[2] = __builtin_amdgcn_perm(b23, a23, 0x05040100u);
+  t.lo[3] = __builtin_amdgcn_perm(b23, a23, 0x07060302u);
+  if (QBITS == 3) {
+    const uint32_t M4 = M << 2, nM4 = 0x01010100u - M4;                // 4m <= 124
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t sg = (rc.s >> (4 * g)) & 15u;
-    t.lo[g] = lut2(sg);
-    t.hi[g] = QBITS == 3 ? lut_hi(sg) : 0u;
+    for (int g = 0; g < 4; ++g)                                         // -4m 4m
+      t.hi[g] = __builtin_amdgcn_perm(M4, nM4, uint32_t(g) | (uint32_t(4 + g) << 8));
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) t.hi[g] = 0u;
   }
   return t;
 }
 
-// A operand of MFMA n (run 8h + n of the lane's row): the low-bit integers,
-// and for 3-bit codes the third-bit integers in G.
+// Weight operand of MFMA n (run 8h + n of the lane's row): the low-bit
+// integers, and for 3-bit codes the third-bit integers in G.
 template <int QBITS>
-__device__ inline void row_operand(const RowCodes& rc, const RowLuts<QBITS>& t, int n, v4i& A,
+__device__ inline void row_operand(const RowCodes& rc, const RowLuts<QBITS>& t, int n, v4i& W,
                                    v4i& G) {
-  A = dequant_dword(n < 4 ? sel_u4(rc.lo, n) : sel_u4(rc.hi, n - 4), t.lo[n >> 1]);
+  W = dequant_dword(n < 4 ? sel_u4(rc.lo, n) : sel_u4(rc.hi, n - 4), t.lo[n >> 1]);
   if (QBITS == 3) {
     const uint32_t bits = (sel_u4(rc.hb, n >> 1) >> (16 * (n & 1))) & 0xffffu;
     G = dequant_hi16(bits, t.hi[n >> 1]);
@@ -157,11 +181,11 @@ __device__ inline void row_operand(const RowCodes& rc, const RowLuts<QBITS>& t, 
 }
 
 template <bool GATEUP, int QBITS>
-__global__ __launch_bounds__(512) void prefill_expert32_kernel(
+__global__ __launch_bounds__(512) void prefill_expert_kernel(
     PoolView pv, int H, int F, int k, const uint8_t* __restrict__ aq,
     const int32_t* __restrict__ ae, const uint32_t* __restrict__ early_out,
-    const int32_t* __restrict__ n_items_p, const int32_t* __restrict__ tile_bucket,
-    const int32_t* __restrict__ tile_start, const int32_t* __restrict__ bucket_start,
+    const int32_t* __restrict__ n_items_p, const int32_t* __restrict__ item_bucket,
+    const int32_t* __restrict__ item_start, const int32_t* __restrict__ bucket_start,
     const int32_t* __restrict__ bucket_slot, const int32_t* __restrict__ pairs,
     float* __restrict__ out) {
   if (*early_out) return;
@@ -171,162 +195,187 @@ __global__ __launch_bounds__(512) void prefill_expert32_kernel(
   __shared__ __align__(16) uint8_t s_b[kPassTok * (8 * 1024 + 144)];
   __shared__ int s_src[kPassTok];     // operand row of each pass token (-1: none)
   __shared__ int s_dst[kPassTok];     // output row
-  __shared__ int s_e[kPassTok * 8];   // exponent of (token, K-block)
-  __shared__ __align__(16) float s_rs[8][32];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  __shared__ float s_cs[kPassTok];    // 2^-e of the token's operand row
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = GATEUP ? H : F;
   const int NR = GATEUP ? F : H;
   const int KB = K / 256, kbs = __builtin_ctz(KB);
   const int tstride = KB * 1024 + 144;
   const int NTI = GATEUP ? NR / 16 : NR / 32;     // 32-row tiles per item
-  const int NQ = (NTI / 8) * KB;                   // (tile, K-block) steps of a wave
-  const int h = l >> 5, lr = l & 31;               // A: row lr of the tile, K-half h
-  const int tcol = lr >> 2, dcol = l & 3;          // B/D: token and digit of column lr
+  const int RPI = NTI / 8;                         // rounds per item
+  const int h = l >> 5, c = l & 31;
   constexpr int NPF = QBITS == 3 ? 2 : 4;          // code blocks in flight
   const int n_items = *n_items_p;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int b = tile_bucket[item];
-    const int p0 = bucket_start[b], n = bucket_start[b + 1] - p0;
-    const int c0 = (item - tile_start[b]) * kPassTok;
-    const int nt = n - c0 < kPassTok ? n - c0 : kPassTok;
-    const int slot = bucket_slot[b];
-    // the wave's A stream: step q = (tile i = q >> kbs, K-block q & (KB-1));
-    // tile i is row tile w + 8i: gate/up rows 16(w+8i) .. +15 of gate (lanes
-    // lr < 16) and of up (lr >= 16); down rows 32(w+8i) + lr
-    const uint8_t* tA = tensor_base(pv, slot, GATEUP ? (lr < 16 ? 0 : 1) : 2);
-    auto blk_of = [&](int q) {
-      const int tt = w + 8 * (q >> kbs);
-      const int row = GATEUP ? 16 * tt + (lr & 15) : 32 * tt + lr;
-      return int64_t(row) * KB + (q & (KB - 1));
+  const int64_t R = int64_t(n_items) * RPI;
+  const int r0 = int(R * blockIdx.x / gridDim.x);
+  const int r1 = int(R * (blockIdx.x + 1) / gridDim.x);
+  if (r0 >= r1) return;
+  const int NQ = (r1 - r0) * KB;                   // (round, K-block) steps
+
+  // The wave's code stream: round r's tile is (r % RPI) * 8 + w of item
+  // r / RPI; the lane's row in it is 16 * tile + c%16 of gate (c < 16) or
+  // up (c >= 16), or 32 * tile + c of down.
+  const int which = GATEUP ? (c < 16 ? 0 : 1) : 2;
+  const int rowoff = GATEUP ? (c & 15) : c;
+  constexpr int ROWS = GATEUP ? 16 : 32;
+  const uint32_t ssel = h ? 0x03030202u : 0x01010000u;
+  // Past the end of the range the stream keeps loading its last block, so
+  // every ring slot is refilled at every step (no data-dependent refills,
+  // which would make the compiler copy the ring and wait for it).
+  int s_item = r0 / RPI, s_tile = (r0 - s_item * RPI) * 8 + w, s_kb = 0, s_left = NQ;
+  const uint8_t* s_t = tensor_base(pv, bucket_slot[item_bucket[s_item]], which);
+  auto next_codes = [&]() {
+    const RowCodes rc =
+        load_row_codes<QBITS>(s_t, pv, int64_t(ROWS * s_tile + rowoff) * KB + s_kb, h);
+    if (--s_left <= 0) return rc;
+    if (++s_kb == KB) {
+      s_kb = 0;
+      s_tile += 8;
+      if (s_tile >= NTI) {
+        s_tile -= NTI;
+        if (++s_item < n_items) s_t = tensor_base(pv, bucket_slot[item_bucket[s_item]], which);
+      }
+    }
+    return rc;
+  };
+  // A ring of NPF code blocks in flight in NPF + 1 slots: step ip uses slot
+  // ip and refills slot ip - 1, the one the previous step finished with, so
+  // no load targets a register that is still being read and the unrolled
+  // loop keeps every slot in fixed registers.
+  constexpr int NS = NPF + 1;
+  RowCodes pf[NS];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf[i] = next_codes();
+
+  int staged = -1;                       // item whose operands are in LDS
+  int item = 0, tile = 0;                // the current round's item and this wave's tile
+  float acc[kCT][4];
+  for (int q0 = 0; q0 < NQ; q0 += NS)
+#pragma unroll
+  for (int ip = 0; ip < NS; ++ip) {
+    const int q = q0 + ip;
+    const RowCodes& ca = pf[ip];
+    pf[(ip + NPF) % NS] = next_codes();  // on every path, so the ring stays in place
+    if (q >= NQ) continue;
+    const int kb = q & (KB - 1);
+    if (kb == 0) {
+      const int r = r0 + (q >> kbs);
+      item = r / RPI;
+      tile = (r - item * RPI) * 8 + w;
+      if (item != staged) {
+        // every wave reaches this step together (same rounds, same K-blocks)
+        __syncthreads();                 // the previous item's operands are no longer read
+        const int b = item_bucket[item];
+        const int p0 = bucket_start[b], n = bucket_start[b + 1] - p0;
+        const int c0 = (item - item_start[b]) * kPassTok;
+        const int nt = n - c0 < kPassTok ? n - c0 : kPassTok;
+        if (tid < kPassTok) {
+          const int pos = p0 + c0 + tid;
+          const int src = tid < nt ? (GATEUP ? pairs[pos] / k : pos) : -1;
+          s_src[tid] = src;
+          s_dst[tid] = tid < nt ? (GATEUP ? pos : pairs[pos]) : -1;
+          s_cs[tid] = src >= 0 ? ldexpf(1.f, -ae[int64_t(src) * KB]) : 0.f;
+        }
+        __syncthreads();
+        // wave w copies tokens TPW*w .. TPW*w + TPW-1, one 1 KiB K-block per
+        // instruction; absent tokens are skipped (their rows are never stored)
+        constexpr int TPW = kPassTok / 8;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int t = TPW * w + u;
+          const int src = __builtin_amdgcn_readfirstlane(s_src[t]);
+          if (src >= 0) {
+            const uint8_t* g = aq + int64_t(src) * KB * 1024 + 16 * l;
+            uint8_t* d = &s_b[t * tstride];
+            for (int j = 0; j < KB; ++j)
+              __builtin_amdgcn_global_load_lds(g + j * 1024, d + j * 1024, 16, 0, 0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        staged = item;
+      }
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[ct][m] = 0.f;
+    }
+    const RowLuts<QBITS> luts = row_luts<QBITS>(ca, ssel);
+    // the lane's row's block factor: half (block parity) of the d dword
+    const float rs = dh_dq<QBITS>((KB == 1 ? rowoff & 1 : kb & 1) ? ca.dh >> 16 : ca.dh & 0xffffu);
+    v16i D[kCT];
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) D[ct] = v16i{};
+    // digit operands read one MFMA step ahead, so no MFMA waits on its own
+    // LDS read.  Chunk of token c/4, digit c%4, run 8h + nn: 512h + 64(c%4) +
+    // 256(nn/4) + 16(nn%4) bytes into the token's K-block.
+    const uint8_t* abase = &s_b[(c >> 2) * tstride + kb * 1024 + 512 * h + 64 * (c & 3)];
+    auto aread = [&](int nn, int ct) {
+      const int4 v = *reinterpret_cast<const int4*>(abase + 8 * ct * tstride +
+                                                    256 * (nn >> 2) + 16 * (nn & 3));
+      return v4i{v.x, v.y, v.z, v.w};
     };
-    __syncthreads();                       // the previous item is done with LDS
-    if (tid < kPassTok) {
-      const int pos = p0 + c0 + tid;
-      s_src[tid] = tid < nt ? (GATEUP ? pairs[pos] / k : pos) : -1;
-      s_dst[tid] = tid < nt ? (GATEUP ? pos : pairs[pos]) : -1;
-    }
-    RowCodes pf[NPF];                      // a ring of code blocks in flight
+    v4i Ad[2][kCT];
 #pragma unroll
-    for (int i = 0; i < NPF; ++i)
-      if (i < NQ) pf[i] = load_row_codes<QBITS>(tA, pv, blk_of(i), h);
-    __syncthreads();
-    // operands straight from memory to LDS: wave w copies tokens
-    // kPassTok/8 * w .. +kPassTok/8 - 1, one 1 KiB K-block per instruction;
-    // absent tokens are skipped (their columns are never stored)
-    constexpr int TPW = kPassTok / 8;
+    for (int ct = 0; ct < kCT; ++ct) Ad[0][ct] = aread(0, ct);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = TPW * w + u;
-      const int src = __builtin_amdgcn_readfirstlane(s_src[t]);
-      if (src >= 0) {
-        const uint8_t* g = aq + int64_t(src) * KB * 1024 + 16 * l;
-        uint8_t* d = &s_b[t * tstride];
-        for (int kb = 0; kb < KB; ++kb)
-          __builtin_amdgcn_global_load_lds(g + kb * 1024, d + kb * 1024, 16, 0, 0);
+    for (int nn = 0; nn < 8; ++nn) {
+      if (nn < 7) {
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) Ad[(nn + 1) & 1][ct] = aread(nn + 1, ct);
       }
-      if (l < KB) s_e[t * 8 + l] = src >= 0 ? ae[int64_t(src) * KB + l] : 0;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    float acc[kCT][16];
-    for (int q0 = 0; q0 < NQ; q0 += NPF)
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's MFMAs
+      v4i W, G;
+      row_operand<QBITS>(ca, luts, nn, W, G);
 #pragma unroll
-    for (int ip = 0; ip < NPF; ++ip) {
-      const int q = q0 + ip;
-      if (q >= NQ) break;
-      const int kb = q & (KB - 1);
-      const RowCodes ca = pf[ip];
-      if (q + NPF < NQ) pf[ip] = load_row_codes<QBITS>(tA, pv, blk_of(q + NPF), h);
-      if (kb == 0) {
+      for (int ct = 0; ct < kCT; ++ct) {
+        D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ad[nn & 1][ct], W, D[ct], 0, 0, 0);
+        if (QBITS == 3)
+          D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ad[nn & 1][ct], G, D[ct], 0, 0, 0);
+      }
+    }
+    // X = 2^24 D0 + 2^16 D1 + 2^8 D2 + D3 (digit 0 most significant): the
+    // pairs 256 D0 + D1 and 256 D2 + D3 stay below 2^31, so each token takes
+    // two conversions and one scaled add per block
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int hi = D[ct][4 * m] * 256 + D[ct][4 * m + 1];
+        const int lo = D[ct][4 * m + 2] * 256 + D[ct][4 * m + 3];
+        acc[ct][m] = fmaf(fmaf(float(hi), 65536.f, float(lo)), rs, acc[ct][m]);
+      }
+    if (kb == KB - 1) {
+      // tile done: the lane holds row c of the tile for tokens 8ct + 2m + h
+      float v[kCT][4];
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[ct][m] = acc[ct][m] * s_cs[8 * ct + 2 * m + h];
+      if (GATEUP) {
+        // gate lanes (c < 16) finish tokens m = 0, 1 and up lanes m = 2, 3
+        const bool gl = c < 16;
+        const int j = 16 * tile + (c & 15);
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
-      }
-      if (h == 0) s_rs[w][lr] = dh_dq<QBITS>(ca.dh);   // row scales through LDS
-      wave_lds_sync32();
-      const RowLuts<QBITS> luts = row_luts<QBITS>(ca);
-      v16i D[kCT];
-#pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) D[ct] = v16i{};
-      // B operands read one MFMA step ahead, so no MFMA waits on its own LDS
-      // read.  Chunk of run 8h + nn, digit dcol: 512h + 64dcol + 256(nn/4) +
-      // 16(nn%4) bytes into the token's K-block.
-      const uint8_t* bbase = &s_b[tcol * tstride + kb * 1024 + 512 * h + 64 * dcol];
-      auto bread = [&](int nn, int ct) {
-        const int4 v = *reinterpret_cast<const int4*>(bbase + 8 * ct * tstride +
-                                                      256 * (nn >> 2) + 16 * (nn & 3));
-        return v4i{v.x, v.y, v.z, v.w};
-      };
-      v4i Bc[2][kCT];
-#pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) Bc[0][ct] = bread(0, ct);
-#pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        if (nn < 7) {
-#pragma unroll
-          for (int ct = 0; ct < kCT; ++ct) Bc[(nn + 1) & 1][ct] = bread(nn + 1, ct);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's MFMAs
-        v4i A, G;
-        row_operand<QBITS>(ca, luts, nn, A, G);
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
-          D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bc[nn & 1][ct], D[ct], 0, 0, 0);
-          if (QBITS == 3)
-            D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(G, Bc[nn & 1][ct], D[ct], 0, 0, 0);
-        }
-      }
-      // row factor d/32 (or d/64); the column factor 2^(8(3-digit) - e) is one
-      // per token (a row exponent) and applied when the tile is done
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 f = *reinterpret_cast<const float4*>(&s_rs[w][8 * g + 4 * h]);
-        const float rv[4] = {f.x, f.y, f.z, f.w};
+          for (int i = 0; i < 2; ++i) {
+            const float other = __shfl_xor(gl ? v[ct][2 + i] : v[ct][i], 16);
+            const int m = gl ? i : 2 + i;
+            const float hv = gl ? silu_mul(v[ct][i], other) : silu_mul(other, v[ct][2 + i]);
+            const int dst = s_dst[8 * ct + 2 * m + h];
+            if (dst >= 0) out[int64_t(dst) * F + j] = hv;
+          }
+      } else {
+        const int i0 = 32 * tile + c;
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[ct][4 * g + j] = fmaf(float(D[ct][4 * g + j]), rv[j], acc[ct][4 * g + j]);
-      }
-      wave_lds_sync32();                   // row scales read before the next step's
-      if (kb == KB - 1) {
-        // tile done: combine each token's four digit columns (lanes
-        // 4*tcol .. +3) and store
-        const int tt = w + 8 * (q >> kbs);
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
-          const int dst = s_dst[8 * ct + tcol];
-          const float cs = ldexpf(1.f, 8 * (3 - dcol) - s_e[(8 * ct + tcol) * 8]);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float x = acc[ct][v] * cs;
-            x += quad_swap<0xb1>(x);          // quad_perm [1,0,3,2]
-            x += quad_swap<0x4e>(x);          // quad_perm [2,3,0,1]
-            acc[ct][v] = x;
+          for (int m = 0; m < 4; ++m) {
+            const int dst = s_dst[8 * ct + 2 * m + h];
+            if (dst >= 0) out[int64_t(dst) * H + i0] = v[ct][m];
           }
-          if (dcol == 0 && dst >= 0) {
-            if (GATEUP) {                  // rows R = 8g + 4h + j < 16: gate; R + 16: up
-              const int j0 = 16 * tt;
-#pragma unroll
-              for (int g = 0; g < 2; ++g) {
-                float4 hv;
-                hv.x = silu_mul(acc[ct][4 * g + 0], acc[ct][4 * g + 8]);
-                hv.y = silu_mul(acc[ct][4 * g + 1], acc[ct][4 * g + 9]);
-                hv.z = silu_mul(acc[ct][4 * g + 2], acc[ct][4 * g + 10]);
-                hv.w = silu_mul(acc[ct][4 * g + 3], acc[ct][4 * g + 11]);
-                *reinterpret_cast<float4*>(out + int64_t(dst) * F + j0 + 8 * g + 4 * h) = hv;
-              }
-            } else {
-              const int i0 = 32 * tt;
-#pragma unroll
-              for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<float4*>(out + int64_t(dst) * H + i0 + 8 * g + 4 * h) =
-                    make_float4(acc[ct][4 * g], acc[ct][4 * g + 1], acc[ct][4 * g + 2],
-                                acc[ct][4 * g + 3]);
-            }
-          }
-        }
       }
     }
   }
@@ -346,20 +395,36 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
                                                                    a.early_out);
 }
 
+// Compute units of the current device (the expert kernels run one block per
+// compute unit); queried once per device.
+static int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  auto kern = a.qbits == 3 ? prefill_expert32_kernel<true, 3> : prefill_expert32_kernel<true, 2>;
-  kern<<<1024, 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
-                             p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
-                             p.pairs, a.hbuf);
+  auto kern = a.qbits == 3 ? prefill_expert_kernel<true, 3> : prefill_expert_kernel<true, 2>;
+  kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
+                                   p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
+                                   p.pairs, a.hbuf);
 }
 
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
-  auto kern = a.qbits == 3 ? prefill_expert32_kernel<false, 3> : prefill_expert32_kernel<false, 2>;
-  kern<<<1024, 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
-                             p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
-                             p.pairs, a.ebuf);
+  auto kern = a.qbits == 3 ? prefill_expert_kernel<false, 3> : prefill_expert_kernel<false, 2>;
+  kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
+                                   p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
+                                   p.pairs, a.ebuf);
 }
 
 }  // namespace rl

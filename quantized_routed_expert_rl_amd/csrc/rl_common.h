@@ -195,7 +195,7 @@ __device__ inline float key_float(uint32_t k) {
 // silu(g) * u = g / (1 + e^-g) * u with the hardware exponential and
 // reciprocal (about 1 ulp each; far inside the float32 tolerance).
 __device__ inline float silu_mul(float g, float u) {
-  return g * __frcp_rn(1.f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
 }
 
 }  // namespace rl

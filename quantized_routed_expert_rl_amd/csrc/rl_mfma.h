@@ -76,7 +76,7 @@ __device__ inline void digit_chunks(const float* v, int e, uint4* chunk) {
 // Byte table of q = (2s+1)(2c-3) for c = 0..3: {-3m, -m, m, 3m}, m = 2s+1.
 __device__ inline uint32_t lut2(uint32_t s) {
   const uint32_t m = 2u * s + 1u;
-  return ((0x10100u - 259u * m) & 0xffffu) | ((m * 0x0301u) << 16);
+  return ((0x10100u - __umul24(259u, m)) & 0xffffu) | (__umul24(m, 0x0301u) << 16);
 }
 
 __device__ inline v4i dequant_dword(uint32_t w, uint32_t lut) {
