@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cache-flushed timings and the HBM read ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
     ap.add_argument("--stacks", action="store_true",
@@ -232,6 +234,13 @@ def main():
         },
     }
 
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        g.replay()
+        return g
+
     # ------------------------------------------------------------ prefill
     if not args.no_prefill:
         w3 = workloads.get("prefill_1l")
@@ -243,13 +252,6 @@ def main():
         s3 = m3.prefill_scratch(T3)
         def chunk():
             m3.prefill(0, X3, w3.plan_cap, r3, s3, Y3)
-
-        def graph_of(fn):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn()
-            g.replay()
-            return g
 
         with torch.cuda.stream(stream):
             for _ in range(2):
@@ -293,6 +295,59 @@ def main():
                          "traffic": stored_traffic("prefill_" + dom),
                          "bytes_per_launch": gb[dom]},
         }
+
+    # ------------------------------------- cold caches and the HBM read ceiling
+    # The figures above are warm: the experts a launch streams may still sit in
+    # the 256 MB Infinity Cache from an earlier replay.  Here each timed run
+    # follows a 512 MiB read-modify-write of another buffer, which evicts them,
+    # and a plain streaming read of 1 GiB gives the ceiling HBM reaches on
+    # this box.
+    if not args.no_cold:
+        flush = torch.zeros(512 << 18, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def cold_ms(fn, reps):
+            tot = 0.0
+            for _ in range(reps):
+                with torch.cuda.stream(stream):
+                    flush.add_(1.0)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                e1.synchronize()
+                tot += e0.elapsed_time(e1)
+            return tot / reps
+
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            lib.moe_decode_layer(C.byref(d), 0, xp[0], W0, None, res, pool, C.byref(outs[0]),
+                                 sp, sb, yp[0], stream.cuda_stream)
+        with torch.cuda.graph(g1, stream=stream):
+            lib.moe_decode_layer(C.byref(d), 0, xp[0], W0, None, res, pool, C.byref(outs[0]),
+                                 sp, sb, yp[0], torch.cuda.current_stream().cuda_stream)
+        g1.replay()
+        cold_tok_ms = cold_ms(g1.replay, 32)
+        with torch.cuda.stream(stream):
+            warm_tok_ms = event_ms(g1.replay, stream, 32)   # the same one-token graph, warm
+        big = torch.ones(1 << 28, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        with torch.cuda.stream(stream):
+            read = lambda: B.rl_stream_read(big, big.numel() * 4, sink, stream.cuda_stream)
+            read()
+            read_ms = event_ms(read, stream, 5)
+        cold = {"decode_us_per_token": round(cold_tok_ms * 1e3, 3),
+                "decode_us_per_token_same_graph_warm": round(warm_tok_ms * 1e3, 3),
+                "decode_tokens_per_s": round(1e3 / cold_tok_ms, 1),
+                "hbm_read_ceiling_gbs": round(big.numel() * 4 / (read_ms * 1e-3) / 1e9, 1),
+                "read_ceiling_kernel": "rl_stream_read over 1 GiB"}
+        if not args.no_prefill:
+            gp = graph_of(chunk)
+            cold_chunk_ms = cold_ms(gp.replay, 5)
+            cold["prefill_ms_per_chunk"] = round(cold_chunk_ms, 4)
+            cold["prefill_tokens_per_s"] = round(T3 / (cold_chunk_ms * 1e-3), 1)
+        line["cold"] = cold
+        del flush, big
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ stacks
     if args.stacks:
@@ -363,12 +418,22 @@ def main():
             n += 1
         cdt = time.perf_counter() - t0
         blas = [i.get("num_threads", 1) for i in threadpool_info()]
+        from threadpoolctl import threadpool_limits
+        n1 = 0
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            while n1 < T and (time.perf_counter() - t1 < args.cpu_seconds / 3 or n1 == 0):
+                O.decode_layer(shape, xs[n1], Wr, None, model.table[0], lambda s: host_pool[s])
+                n1 += 1
+            cdt1 = time.perf_counter() - t1
         line["cpu_baseline"] = {
             "value": round(n / cdt, 3), "unit": "tokens/s", "cores": max(blas + [1]),
             "kind": "oracle",
             "sample": f"first {n} of the {T} decode_1l tokens through oracle.decode_layer "
                       f"({cdt:.1f} s); float64 NumPy, BLAS threads {max(blas + [1])}, "
-                      f"host has {os.cpu_count()} logical CPUs"}
+                      f"host has {os.cpu_count()} logical CPUs",
+            "value_1_thread": round(n1 / cdt1, 3),
+            "sample_1_thread": f"first {n1} tokens with BLAS limited to one thread ({cdt1:.1f} s)"}
     print(json.dumps(line), flush=True)
 
 

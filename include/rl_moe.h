@@ -208,6 +208,15 @@ int rl_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, float* out,
 int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
                     const uint32_t* early_out, void* stream);
 
+/* Measurement helper (not part of the MoE layer): reads `bytes` bytes of the
+ * device buffer `buf` once, in 16-byte words, with a grid of eight blocks
+ * per compute unit, so that the time of the launch gives the HBM read rate
+ * this device reaches with plain streaming loads.  `sink` is a device word
+ * that is written only in the (practically never taken) case that the
+ * folded data equal a fixed constant.  bytes must be a positive multiple of
+ * 16 (RL_E_RANGE); NULL pointers give RL_E_INVAL. */
+int rl_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

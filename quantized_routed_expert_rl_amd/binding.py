@@ -65,6 +65,7 @@ _SIGS = {
                              C.c_void_p]),
     "rl_residual_add": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
+    "rl_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
 }
 
 
@@ -197,3 +198,8 @@ def rl_rmsnorm(n_tokens, hidden, x, out, eps=1e-6, stream=None) -> int:
 def rl_residual_add(n_tokens, hidden, x, y, early_out=None, stream=None) -> int:
     return check(lib.rl_residual_add(n_tokens, hidden, _ptr(x), _ptr(y), _ptr(early_out),
                                      _stream(stream)), "rl_residual_add")
+
+
+def rl_stream_read(buf, nbytes, sink, stream=None) -> int:
+    return check(lib.rl_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+                 "rl_stream_read")

@@ -385,4 +385,16 @@ int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
   return launch_status();
 }
 
+int rl_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return RL_E_INVAL;
+  if (bytes < 16 || bytes % 16) return RL_E_RANGE;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    return RL_E_DEVICE;
+  launch_stream_read(buf, bytes, sink, n_cu, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 }  // extern "C"

@@ -48,4 +48,24 @@ void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t*
   residual_add_kernel<<<int(blocks), 256, 0, st>>>(n, x, y, early_out);
 }
 
+// A plain streaming read: every 16-byte word of buf once, four loads in
+// flight per thread, folded so the loads cannot be dropped; sink is written
+// only if the fold hits a value it never takes in practice.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, int64_t n,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+    acc ^= (a.x ^ b.y ^ c.z ^ d.w) + (a.w ^ b.z ^ c.y ^ d.x);
+  }
+  for (; i < n; i += stride) acc ^= buf[i].x ^ buf[i].w;
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st) {
+  stream_read_kernel<<<8 * n_cu, 256, 0, st>>>(static_cast<const uint4*>(buf), bytes / 16, sink);
+}
+
 }  // namespace rl
