@@ -207,6 +207,13 @@ int rl_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, float* out,
                float eps, void* stream);
 int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
                     const uint32_t* early_out, void* stream);
+/* rl_residual_rmsnorm: the step between two layers in one launch:
+ * x_out[t] = x[t] + y[t] (x_out[t] = x[t] when *early_out != 0; early_out
+ * may be NULL = always add), then a_out[t] = rl_rmsnorm of x_out[t].  x_out
+ * must not overlap x or y.  hidden: a multiple of 256, at most 2048. */
+int rl_residual_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, const float* y,
+                        const uint32_t* early_out, float* x_out, float* a_out, float eps,
+                        void* stream);
 
 /* Measurement helper (not part of the MoE layer): reads `bytes` bytes of the
  * device buffer `buf` once, in 16-byte words, with a grid of eight blocks

@@ -65,6 +65,8 @@ _SIGS = {
                              C.c_void_p]),
     "rl_residual_add": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
+    "rl_residual_rmsnorm": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
     "rl_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
 }
 
@@ -198,6 +200,13 @@ def rl_rmsnorm(n_tokens, hidden, x, out, eps=1e-6, stream=None) -> int:
 def rl_residual_add(n_tokens, hidden, x, y, early_out=None, stream=None) -> int:
     return check(lib.rl_residual_add(n_tokens, hidden, _ptr(x), _ptr(y), _ptr(early_out),
                                      _stream(stream)), "rl_residual_add")
+
+
+def rl_residual_rmsnorm(n_tokens, hidden, x, y, early_out, x_out, a_out, eps=1e-6,
+                        stream=None) -> int:
+    return check(lib.rl_residual_rmsnorm(n_tokens, hidden, _ptr(x), _ptr(y), _ptr(early_out),
+                                         _ptr(x_out), _ptr(a_out), eps, _stream(stream)),
+                 "rl_residual_rmsnorm")
 
 
 def rl_stream_read(buf, nbytes, sink, stream=None) -> int:

@@ -385,6 +385,16 @@ int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
   return launch_status();
 }
 
+int rl_residual_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, const float* y,
+                        const uint32_t* early_out, float* x_out, float* a_out, float eps,
+                        void* stream) {
+  if (!x || !y || !x_out || !a_out) return RL_E_INVAL;
+  if (n_tokens < 1 || hidden < 256 || hidden > 2048 || hidden % 256) return RL_E_RANGE;
+  launch_residual_rmsnorm(n_tokens, hidden, x, y, early_out, x_out, a_out, eps,
+                          static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int rl_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return RL_E_INVAL;
   if (bytes < 16 || bytes % 16) return RL_E_RANGE;

@@ -96,6 +96,9 @@ void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st);
 
 void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st);
+void launch_residual_rmsnorm(int T, int H, const float* x, const float* y,
+                             const uint32_t* early_out, float* x_out, float* a_out, float eps,
+                             hipStream_t st);
 void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,
                          hipStream_t st);
 void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st);

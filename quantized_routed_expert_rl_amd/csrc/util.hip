@@ -7,6 +7,19 @@
 
 namespace rl {
 
+// 1 / sqrt(mean(v^2) + eps) of one token's row, from each thread's float64
+// sum of squares, in every thread of the 256-thread block.
+__device__ inline double block_inv_rms(double s, int H, float eps) {
+  s = wave_sum_f64(s);
+  __shared__ double s_w[4];
+  __shared__ double s_inv;
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) s_inv = 1.0 / sqrt((s_w[0] + s_w[1] + s_w[2] + s_w[3]) / H + double(eps));
+  __syncthreads();
+  return s_inv;
+}
+
 // One block per token: out = x / sqrt(mean(x^2) + eps), the mean of squares
 // accumulated in float64.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* __restrict__ x,
@@ -17,15 +30,38 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* __rest
     const double v = x[base + i];
     s = fma(v, v, s);
   }
-  s = wave_sum_f64(s);
-  __shared__ double s_w[4];
-  __shared__ double s_inv;
-  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) s_inv = 1.0 / sqrt((s_w[0] + s_w[1] + s_w[2] + s_w[3]) / H + double(eps));
-  __syncthreads();
-  const double inv = s_inv;
+  const double inv = block_inv_rms(s, H, eps);
   for (int i = threadIdx.x; i < H; i += 256) out[base + i] = float(double(x[base + i]) * inv);
+}
+
+// The step between two layers of a stack in one launch, one block per token:
+// x_out = x + y (x_out = x when the layer's flag is set), then
+// a_out = rmsnorm(x_out), each thread keeping its own elements in registers.
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
+    int H, const float* __restrict__ x, const float* __restrict__ y,
+    const uint32_t* __restrict__ early_out, float* __restrict__ x_out, float* __restrict__ a_out,
+    float eps) {
+  constexpr int kMaxPer = 8;                     // H <= 2048
+  const int64_t base = int64_t(blockIdx.x) * H;
+  const bool skip = early_out && *early_out;
+  float v[kMaxPer];
+  double s = 0.0;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    if (i < H) {
+      v[u] = skip ? x[base + i] : x[base + i] + y[base + i];
+      x_out[base + i] = v[u];
+      const double d = v[u];
+      s = fma(d, d, s);
+    }
+  }
+  const double inv = block_inv_rms(s, H, eps);
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    if (i < H) a_out[base + i] = float(double(v[u]) * inv);
+  }
 }
 
 __global__ __launch_bounds__(256) void residual_add_kernel(int64_t n, float* __restrict__ x,
@@ -38,6 +74,12 @@ __global__ __launch_bounds__(256) void residual_add_kernel(int64_t n, float* __r
 
 void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st) {
   rmsnorm_kernel<<<T, 256, 0, st>>>(H, x, out, eps);
+}
+
+void launch_residual_rmsnorm(int T, int H, const float* x, const float* y,
+                             const uint32_t* early_out, float* x_out, float* a_out, float eps,
+                             hipStream_t st) {
+  residual_rmsnorm_kernel<<<T, 256, 0, st>>>(H, x, y, early_out, x_out, a_out, eps);
 }
 
 void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,

@@ -6,8 +6,9 @@ x_{l+1} = x_l + y_l, where a layer whose route raised the early-out flag
 adds nothing ("Red Lite dev23 - per-layer early-out", "What changed": every
 kernel downstream of a flagged layer returns at once).  The norm, the MoE
 layer and the residual add all run in librlmoe's kernels; PyTorch only holds
-the buffers and copies x between layers so that each layer's input stays
-available for checking.
+the buffers.  Between two layers one launch (rl_residual_rmsnorm) writes
+x_{l+1} and a_{l+1}, so a layer costs its three (decode) MoE launches plus
+one, and every layer's input stays available for checking.
 
 ``DecodeStack`` runs single tokens through ``moe_decode_layer``;
 ``PrefillStack`` runs a prompt chunk by chunk through ``moe_prefill_chunk``
@@ -37,7 +38,7 @@ class DecodeStack:
         self.model = model
         self.L, self.H = w.n_layers, w.hidden
         self.x = torch.empty(self.L + 1, self.H, device=DEV)
-        self.a = torch.empty(self.L, self.H, device=DEV)
+        self.a = torch.empty(self.L + 1, self.H, device=DEV)   # a[L]: norm of the output
         self.y = torch.empty(self.L, self.H, device=DEV)
         self.routes: List[RouteBuffers] = [
             RouteBuffers.alloc(1, w.top_k, w.n_experts, with_logits=False) for _ in range(self.L)]
@@ -46,11 +47,11 @@ class DecodeStack:
     def token(self, x0: torch.Tensor) -> torch.Tensor:
         """Runs x0 [H] (device) through the stack on the current stream."""
         self.x[0].copy_(x0.reshape(self.H))
+        B.rl_rmsnorm(1, self.H, self.x[0], self.a[0], EPS)
         for l in range(self.L):
-            B.rl_rmsnorm(1, self.H, self.x[l], self.a[l], EPS)
             self.model.decode(l, self.a[l], self.routes[l], self.scratch, self.y[l])
-            self.x[l + 1].copy_(self.x[l])
-            B.rl_residual_add(1, self.H, self.x[l + 1], self.y[l], self.routes[l].early_out)
+            B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
+                                  self.x[l + 1], self.a[l + 1], EPS)
         return self.x[self.L]
 
 
@@ -69,7 +70,7 @@ class PrefillStack:
         T = max(self.chunks)
         self.scratch = model.prefill_scratch(T)
         self.xs = [torch.empty(self.L + 1, n, self.H, device=DEV) for n in self.chunks]
-        self.as_ = [torch.empty(self.L, n, self.H, device=DEV) for n in self.chunks]
+        self.as_ = [torch.empty(self.L + 1, n, self.H, device=DEV) for n in self.chunks]
         self.ys = [torch.empty(self.L, n, self.H, device=DEV) for n in self.chunks]
         self.routes = [[RouteBuffers.alloc(n, w.top_k, w.n_experts, with_logits=False)
                         for _ in range(self.L)] for n in self.chunks]
@@ -81,13 +82,12 @@ class PrefillStack:
         for c, n in enumerate(self.chunks):
             x = self.xs[c]
             x[0].copy_(x0[t0:t0 + n])
+            B.rl_rmsnorm(n, self.H, x[0], self.as_[c][0], EPS)
             for l in range(self.L):
-                B.rl_rmsnorm(n, self.H, x[l], self.as_[c][l], EPS)
                 self.model.prefill(l, self.as_[c][l], self.plan_cap, self.routes[c][l],
                                    self.scratch, self.ys[c][l])
-                x[l + 1].copy_(x[l])
-                B.rl_residual_add(n, self.H, x[l + 1], self.ys[c][l],
-                                  self.routes[c][l].early_out)
+                B.rl_residual_rmsnorm(n, self.H, x[l], self.ys[c][l], self.routes[c][l].early_out,
+                                      x[l + 1], self.as_[c][l + 1], EPS)
             outs.append(x[self.L])
             t0 += n
         return torch.cat(outs)

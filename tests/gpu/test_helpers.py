@@ -1,0 +1,61 @@
+"""The stack helpers and the measurement helper through the C ABI: RMSNorm,
+residual add, the fused residual add + RMSNorm between two layers (with and
+without the layer's early-out flag), and the streaming read, which must leave
+its sink untouched.  The norm is checked against the oracle's float64 norm
+within the float32 tolerance; the residual sums are plain float32 adds and
+must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from gpu.common import close
+from oracle import moe_oracle as O
+from quantized_routed_expert_rl_amd import binding as B
+from quantized_routed_expert_rl_amd.device import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(T, H, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, H)) * rng.uniform(0.1, 10.0, (T, 1))).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,H", [(1, 256), (5, 2048), (3, 768)])
+def test_rmsnorm(T, H):
+    x = _rows(T, H, T * H)
+    out = torch.full((T, H), float("nan"), device="cuda")
+    B.rl_rmsnorm(T, H, to_dev(x), out, 1e-6)
+    close(out.cpu().numpy(), O.rmsnorm(x), "rmsnorm")
+
+
+@pytest.mark.parametrize("flag", [None, 0, 1])
+def test_residual_add(flag):
+    T, H = 4, 1024
+    x, y = _rows(T, H, 1), _rows(T, H, 2)
+    xd = to_dev(x)
+    fl = None if flag is None else torch.tensor([flag], dtype=torch.int32, device="cuda")
+    B.rl_residual_add(T, H, xd, to_dev(y), fl)
+    want = x if flag == 1 else O.residual_add(x, y)
+    assert np.array_equal(xd.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("flag", [None, 0, 1])
+@pytest.mark.parametrize("T,H", [(1, 2048), (7, 512)])
+def test_residual_rmsnorm(flag, T, H):
+    x, y = _rows(T, H, 3 + T), _rows(T, H, 4 + H)
+    fl = None if flag is None else torch.tensor([flag], dtype=torch.int32, device="cuda")
+    xo = torch.full((T, H), float("nan"), device="cuda")
+    ao = torch.full((T, H), float("nan"), device="cuda")
+    B.rl_residual_rmsnorm(T, H, to_dev(x), to_dev(y), fl, xo, ao, 1e-6)
+    want = x if flag == 1 else O.residual_add(x, y)
+    assert np.array_equal(xo.cpu().numpy(), want)
+    close(ao.cpu().numpy(), O.rmsnorm(want), "norm of the residual")
+
+
+def test_stream_read_leaves_sink():
+    buf = torch.ones(1 << 22, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    B.rl_stream_read(buf, buf.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu()[0]) == 7

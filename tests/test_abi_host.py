@@ -89,6 +89,10 @@ def test_errors_before_any_launch():
     assert rc == B.RL_E_SCRATCH                                      # 65 tokens > 64
     assert B.lib.rl_rmsnorm(4, 300, 0x1000, 0x1000, 1e-6, None) == B.RL_E_RANGE
     assert B.lib.rl_residual_add(0, 2048, 0x1000, 0x1000, None, None) == B.RL_E_RANGE
+    assert B.lib.rl_residual_rmsnorm(1, 4096, 0x1000, 0x1000, None, 0x1000, 0x1000, 1e-6,
+                                     None) == B.RL_E_RANGE              # hidden > 2048
+    assert B.lib.rl_residual_rmsnorm(1, 2048, 0x1000, None, None, 0x1000, 0x1000, 1e-6,
+                                     None) == B.RL_E_INVAL
     assert B.lib.rl_stream_read(None, 1 << 20, 0x1000, None) == B.RL_E_INVAL
     assert B.lib.rl_stream_read(0x1000, 1000, 0x1000, None) == B.RL_E_RANGE   # not a multiple of 16
     assert B.lib.rl_strerror(B.RL_E_SCRATCH).decode() == "scratch buffer too small"
