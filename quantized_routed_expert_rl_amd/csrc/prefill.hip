@@ -7,6 +7,7 @@
 // ("Red Lite dev23", "What changed").
 #include "rl_common.h"
 #include "rl_kernels.h"
+#include "rl_select.h"
 
 namespace rl {
 
@@ -182,6 +183,99 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   }
 }
 
+// The whole plan in one block when the chunk forms a single token group
+// (plan_cap >= E) and its pairs fit in LDS.  The pairs are cut into 16
+// consecutive segments, one per wave; per-(segment, expert) counts give each
+// wave its base inside every expert's run, and a wave walks its segment 64
+// pairs at a time, ranking each pair among the equal experts before it in
+// the batch, so every bucket holds its pairs in pair order (stable), exactly
+// as the per-expert scan above.
+constexpr int kFusedMaxPairs = 16384;
+constexpr int kFusedMaxExperts = 1024;
+
+__global__ __launch_bounds__(1024) void plan_fused_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int layer,
+    const int32_t* __restrict__ residency, const uint32_t* __restrict__ early_out, PlanPtrs p,
+    int tile_tokens) {
+  if (*early_out) return;
+  __shared__ int s_ids[kFusedMaxPairs];
+  __shared__ int s_cnt[16][kFusedMaxExperts];   // per (segment, expert): count, then base
+  __shared__ int s_off[kFusedMaxExperts];       // start of each expert's run
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int P = T * k;
+  const int seg = ((P + 15) / 16 + 63) & ~63;   // pairs per segment, whole batches
+  for (int i = tid; i < P; i += 1024) s_ids[i] = ids[i];
+  for (int i = tid; i < 16 * kFusedMaxExperts; i += 1024) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int s0 = wv * seg, s1 = min(P, s0 + seg);
+  for (int i = s0 + lane; i < s1; i += 64) atomicAdd(&s_cnt[wv][s_ids[i]], 1);
+  __syncthreads();
+  // per expert: total count and each segment's base inside the expert's run
+  int total = 0;
+  if (tid < E) {
+    for (int w = 0; w < 16; ++w) {
+      const int c = s_cnt[w][tid];
+      s_cnt[w][tid] = total;
+      total += c;
+    }
+  }
+  int v[3] = {total, total > 0 ? 1 : 0, (total + tile_tokens - 1) / tile_tokens};
+  int tot[3];
+  block_scan3(v, tot);
+  if (tid < E) {
+    p.counts[tid] = total;
+    p.offs[tid] = v[0];
+    s_off[tid] = v[0];
+    if (total > 0) {
+      const int b = v[1];
+      p.bucket_expert[b] = tid;
+      p.bucket_start[b] = v[0];
+      p.bucket_slot[b] = residency[int64_t(layer) * E + tid];
+      p.tile_start[b] = v[2];
+      for (int u = 0; u < (total + tile_tokens - 1) / tile_tokens; ++u) p.tile_bucket[v[2] + u] = b;
+    }
+  }
+  if (tid == 0) {
+    *p.n_groups = 1;
+    p.group_bounds[0] = 0;
+    p.group_bounds[1] = T;
+    *p.n_buckets = tot[1];
+    p.group_bucket_start[0] = 0;
+    p.group_bucket_start[1] = tot[1];
+    p.bucket_start[tot[1]] = tot[0];
+    p.tile_start[tot[1]] = tot[2];
+    *p.n_tiles = tot[2];
+  }
+  __syncthreads();
+  // stable scatter, wave wv over its segment in order.  Per batch the high
+  // half of s_cnt[wv][e] counts the batch's pairs of expert e (LDS adds, so
+  // the count is exact whatever order the lanes are served in); a pair whose
+  // expert is unique in the batch has rank 0, and only repeated experts are
+  // ranked by ballots, one distinct expert per round.
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int b0 = s0; b0 < s1; b0 += 64) {
+    const int i = b0 + lane;
+    const bool live = i < s1;
+    const int e = live ? s_ids[i] : 0;
+    if (live) atomicAdd(&s_cnt[wv][e], 1 << 16);
+    wave_lds_sync();
+    const int cb = live ? s_cnt[wv][e] : 0;
+    const int cnt = cb >> 16, base = cb & 0xffff;
+    int rank = 0;
+    unsigned long long todo = __ballot(cnt > 1);
+    while (todo) {
+      const int e0 = __builtin_amdgcn_readlane(e, __builtin_ctzll(todo));
+      const unsigned long long m = __ballot(live && e == e0);
+      if (live && e == e0) rank = __popcll(m & below);
+      todo &= ~m;
+    }
+    if (live) p.pairs[s_off[e] + base + rank] = i;
+    wave_lds_sync();
+    if (live && rank == cnt - 1) s_cnt[wv][e] = base + cnt;   // the batch's last pair of e
+    wave_lds_sync();
+  }
+}
+
 // ---------------------------------------------------- batched experts
 // Bucket of a token tile: last b with tile_start[b] <= tile.
 __device__ inline int find_tile_bucket(const int32_t* tile_start, int nb, int tile) {
@@ -353,6 +447,11 @@ __global__ __launch_bounds__(256) void prefill_sum_kernel(
 // ------------------------------------------------------------ launchers
 void launch_prefill_plan(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
+  if (a.plan_cap >= a.E && a.T * a.k <= kFusedMaxPairs && a.E <= kFusedMaxExperts) {
+    plan_fused_kernel<<<1, 1024, 0, st>>>(a.ids, a.T, a.k, a.E, a.layer, a.residency,
+                                          a.early_out, p, a.tile_tokens);
+    return;
+  }
   plan_groups_kernel<<<1, 64, 0, st>>>(a.ids, a.T, a.k, a.E, a.plan_cap, a.early_out,
                                        p.n_groups, p.group_bounds);
   const int blocks = (a.E + 15) / 16;
