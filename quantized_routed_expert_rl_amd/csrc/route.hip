@@ -18,10 +18,12 @@ namespace rl {
 // logits[t][e] = fl32(sum_i W[e][i] x[t][i] + b[e]) on the float64 matrix
 // cores (v_mfma_f64_16x16x4f64; A lane l: row l%16, K index l/16; B lane l:
 // column l%16, K index l/16; output lane l, v: row l/16 + 4v, column l%16).
-// Block = 32 tokens x 32 experts, one 16x16 tile per wave; K runs in
-// 64-value chunks staged through LDS (double buffer; the next chunk's
-// float4 loads are in flight while the current one computes), so each x and
-// W value is read from memory once per block instead of once per wave.
+// Block = 32 tokens x 32 experts, one 16x16 tile per wave pair: waves w and
+// w + 4 take the two halves of K, so two waves share each SIMD and hide each
+// other's LDS and memory latency, and the halves are added in float64 at the
+// end.  Each half runs in 64-value chunks staged through LDS (double buffer;
+// the next chunk's float4 loads are in flight while the current one
+// computes), so each x and W value is read from memory once per block.
 // Inside each 16-value group g of a chunk, MFMA step 4g+i of lane quad kq
 // takes K index 16g + 4kq + i for both operands: one float4 LDS read per
 // lane per group.  Four accumulation chains (one per group) keep the matrix
@@ -30,24 +32,27 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr int kRgStride = 68;   // floats per staged row: 64 + 4 keeps float4 reads conflict-free
 
-__global__ __launch_bounds__(256) void route_gemm_kernel(
+__global__ __launch_bounds__(512) void route_gemm_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
     int T, int E, int H, float* __restrict__ logits, float* __restrict__ logits_out,
     uint32_t* miss_count, uint32_t* early_out) {
-  __shared__ __align__(16) float s_a[2][32 * kRgStride];   // tokens
-  __shared__ __align__(16) float s_b[2][32 * kRgStride];   // experts
-  const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+  __shared__ __align__(16) float s_a[2][2][32 * kRgStride];   // [K half][buffer] tokens
+  __shared__ __align__(16) float s_b[2][2][32 * kRgStride];   // [K half][buffer] experts
+  __shared__ v4d s_part[4][64];                               // upper half's sums
+  const int tid = threadIdx.x, l = tid & 63, wv = (tid >> 6) & 3, kh = tid >> 8;
   const int tb = blockIdx.y * 32, eb = blockIdx.x * 32;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     *miss_count = 0u;
     *early_out = 0u;
   }
-  // staging: thread tid copies row tid/8, floats 8*(tid%8) .. +7 of the chunk
-  // for both operands (two float4 each)
-  const int sr = tid >> 3, sc = 8 * (tid & 7);
+  // staging: thread copies row (tid%256)/8, floats 8*(tid%8) .. +7 of its
+  // half's chunk for both operands (two float4 each)
+  const int st = tid & 255, sr = st >> 3, sc = 8 * (st & 7);
+  const int nch = H / 128;                                     // chunks per K half
+  const int k0 = kh * (H / 2);
   const bool va = tb + sr < T, vb = eb + sr < E;
-  const float* ga = x + int64_t(va ? tb + sr : 0) * H + sc;
-  const float* gb = W + int64_t(vb ? eb + sr : 0) * H + sc;
+  const float* ga = x + int64_t(va ? tb + sr : 0) * H + k0 + sc;
+  const float* gb = W + int64_t(vb ? eb + sr : 0) * H + k0 + sc;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 pa0 = va ? *reinterpret_cast<const float4*>(ga) : z4;
   float4 pa1 = va ? *reinterpret_cast<const float4*>(ga + 4) : z4;
@@ -58,13 +63,14 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(
   v4d acc4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc4[u] = v4d{0.0, 0.0, 0.0, 0.0};
-  const int nch = H / 64;
   for (int ch = 0; ch < nch; ++ch) {
     const int buf = ch & 1;
-    *reinterpret_cast<float4*>(&s_a[buf][sr * kRgStride + sc]) = pa0;
-    *reinterpret_cast<float4*>(&s_a[buf][sr * kRgStride + sc + 4]) = pa1;
-    *reinterpret_cast<float4*>(&s_b[buf][sr * kRgStride + sc]) = pb0;
-    *reinterpret_cast<float4*>(&s_b[buf][sr * kRgStride + sc + 4]) = pb1;
+    float* sa = s_a[kh][buf];
+    float* sb = s_b[kh][buf];
+    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc]) = pa0;
+    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc + 4]) = pa1;
+    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc]) = pb0;
+    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc + 4]) = pb1;
     __syncthreads();
     if (ch + 1 < nch) {
       const int off = (ch + 1) * 64;
@@ -76,8 +82,8 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(
     float4 av[4], bv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      av[g] = *reinterpret_cast<const float4*>(&s_a[buf][ra * kRgStride + 16 * g + 4 * kq]);
-      bv[g] = *reinterpret_cast<const float4*>(&s_b[buf][rb * kRgStride + 16 * g + 4 * kq]);
+      av[g] = *reinterpret_cast<const float4*>(&sa[ra * kRgStride + 16 * g + 4 * kq]);
+      bv[g] = *reinterpret_cast<const float4*>(&sb[rb * kRgStride + 16 * g + 4 * kq]);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -92,7 +98,11 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(
     for (int g = 0; g < 4; ++g)
       acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].w), double(bv[g].w), acc4[g], 0, 0, 0);
   }
-  const v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  if (kh == 1) s_part[wv][l] = acc;
+  __syncthreads();
+  if (kh == 1) return;
+  acc += s_part[wv][l];
   const int t0 = tb + (wv >> 1) * 16, e0 = eb + (wv & 1) * 16;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -144,7 +154,7 @@ int cand_per_lane(int E) {
 
 void launch_route(const RouteArgs& a, hipStream_t st) {
   dim3 grid((a.E + 31) / 32, (a.T + 31) / 32);
-  route_gemm_kernel<<<grid, 256, 0, st>>>(a.x, a.W, a.bias, a.T, a.E, a.H, a.logits,
+  route_gemm_kernel<<<grid, 512, 0, st>>>(a.x, a.W, a.bias, a.T, a.E, a.H, a.logits,
                                           a.logits_out, a.miss_count, a.early_out);
   switch (cand_per_lane(a.E)) {
     case 1: launch_topk_n<1>(a, st); break;
