@@ -215,6 +215,65 @@ int rl_residual_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, const 
                         const uint32_t* early_out, float* x_out, float* a_out, float eps,
                         void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert cache (host memory and host code only; no device calls).
+ * A bounded pool of n_slots expert slots serves n_layers x n_experts keys.
+ * The cache decides which slot a missing expert is loaded into and which
+ * resident expert that evicts; the caller copies the expert's bytes into the
+ * slot and mirrors the cache's table into the device residency table
+ * ("Red Lite dev21 - GPU-routed decode", "What changed": the residency table
+ * is maintained on every LRU commit and abort, and a reservation reports the
+ * key a miss evicts).  Least recently used replacement; all hits of a
+ * selection are reserved before any victim is chosen, so a selection never
+ * evicts one of its own experts ("Red Lite dev20 - batched prompt
+ * ingestion", the LRU fix).  Every load into a slot bumps that slot's load
+ * generation ("Red Lite dev23", "What changed", per-slot load generations):
+ * a caller that recorded generations when it planned work on some slots can
+ * tell whether any of them was reloaded since.  One reservation may be open
+ * at a time; the cache is not thread-safe.  Keys are layer * n_experts +
+ * expert.
+ *
+ * rl_cache_create: NULL if a count is < 1, n_layers * n_experts > 2^30 or
+ *   memory runs out.  All slots start free (used before any eviction).
+ * rl_cache_insert: make (layer, expert) resident in a free slot (for seeding
+ *   from an initial residency table); RL_E_INVAL if the key is resident, the
+ *   slot is taken or a reservation is open; RL_E_RANGE for bad indices.
+ * rl_cache_lookup: the key's slot, or -1.
+ * rl_cache_reserve: the k ids (host array) of one layer's selection; writes
+ *   per id its slot, load[i] = 1 if the caller must copy the expert into that
+ *   slot, evicted[i] = the key the load displaces (-1: the slot was free or
+ *   no load), and (if gens != NULL) the slot's load generation.  Returns the
+ *   number of loads (>= 0), RL_E_RANGE (bad layer/id, k < 1, or more misses
+ *   than slots outside the selection: the cache is then unchanged) or
+ *   RL_E_INVAL (NULL pointer, or a reservation already open).
+ * rl_cache_touch: the resident ones of a layer's k ids become the most
+ *   recently used (the first id most recent), as after the device used them
+ *   without any load; returns how many were resident, RL_E_RANGE for a bad
+ *   layer or id (ids before it may have been touched), RL_E_INVAL while a
+ *   reservation is open.
+ * rl_cache_commit: the reservation's slots become the most recently used
+ *   (the first id most recent) and the reservation closes.
+ * rl_cache_abort: keys return to the slots they held before the reservation
+ *   (load generations stay bumped) and the reservation closes.
+ * rl_cache_generation: load generation of a slot (0 for a bad slot).
+ * rl_cache_table: writes the [n_layers x n_experts] int32 table of slots
+ *   (-1 = not resident) into a host array, for the device residency table.
+ * rl_cache_stats: out[5] = reservations, hits, misses (= loads), evictions,
+ *   aborted reservations. */
+typedef struct rl_cache rl_cache;
+rl_cache* rl_cache_create(int32_t n_slots, int32_t n_layers, int32_t n_experts);
+void rl_cache_destroy(rl_cache* c);
+int rl_cache_insert(rl_cache* c, int32_t layer, int32_t expert, int32_t slot);
+int32_t rl_cache_lookup(const rl_cache* c, int32_t layer, int32_t expert);
+int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, int32_t* slots,
+                     int32_t* load, int32_t* evicted, uint32_t* gens);
+int rl_cache_touch(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k);
+int rl_cache_commit(rl_cache* c);
+int rl_cache_abort(rl_cache* c);
+uint32_t rl_cache_generation(const rl_cache* c, int32_t slot);
+int rl_cache_table(const rl_cache* c, int32_t* table);
+int rl_cache_stats(const rl_cache* c, int64_t* out);
+
 /* Measurement helper (not part of the MoE layer): reads `bytes` bytes of the
  * device buffer `buf` once, in 16-byte words, with a grid of eight blocks
  * per compute unit, so that the time of the launch gives the HBM read rate

@@ -68,6 +68,18 @@ _SIGS = {
     "rl_residual_rmsnorm": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
     "rl_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "rl_cache_create": (C.c_void_p, [C.c_int32, C.c_int32, C.c_int32]),
+    "rl_cache_destroy": (None, [C.c_void_p]),
+    "rl_cache_insert": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32]),
+    "rl_cache_lookup": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32]),
+    "rl_cache_reserve": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rl_cache_touch": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32]),
+    "rl_cache_commit": (C.c_int, [C.c_void_p]),
+    "rl_cache_abort": (C.c_int, [C.c_void_p]),
+    "rl_cache_generation": (C.c_uint32, [C.c_void_p, C.c_int32]),
+    "rl_cache_table": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "rl_cache_stats": (C.c_int, [C.c_void_p, C.c_void_p]),
 }
 
 
@@ -212,3 +224,68 @@ def rl_residual_rmsnorm(n_tokens, hidden, x, y, early_out, x_out, a_out, eps=1e-
 def rl_stream_read(buf, nbytes, sink, stream=None) -> int:
     return check(lib.rl_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
                  "rl_stream_read")
+
+
+class ExpertCache:
+    """The library's host-side expert cache (rl_cache_*): argument
+    marshalling only."""
+
+    def __init__(self, n_slots: int, n_layers: int, n_experts: int):
+        self.n_slots, self.n_layers, self.n_experts = n_slots, n_layers, n_experts
+        self.h = lib.rl_cache_create(n_slots, n_layers, n_experts)
+        if not self.h:
+            raise RlError("rl_cache_create failed")
+
+    def close(self):
+        if self.h:
+            lib.rl_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
+
+    def insert(self, layer: int, expert: int, slot: int):
+        check(lib.rl_cache_insert(self.h, layer, expert, slot), "rl_cache_insert")
+
+    def lookup(self, layer: int, expert: int) -> int:
+        return lib.rl_cache_lookup(self.h, layer, expert)
+
+    def reserve(self, layer: int, ids):
+        """-> (n_loads, slots, load, evicted, gens) as numpy arrays; raises on error."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        k = ids.size
+        slots = np.empty(k, np.int32)
+        load = np.empty(k, np.int32)
+        evicted = np.empty(k, np.int32)
+        gens = np.empty(k, np.uint32)
+        n = lib.rl_cache_reserve(self.h, layer, ids.ctypes.data, k, slots.ctypes.data,
+                                 load.ctypes.data, evicted.ctypes.data, gens.ctypes.data)
+        check(min(n, 0), "rl_cache_reserve")
+        return n, slots, load, evicted, gens
+
+    def touch(self, layer: int, ids) -> int:
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        return check(lib.rl_cache_touch(self.h, layer, ids.ctypes.data, ids.size), "rl_cache_touch")
+
+    def commit(self):
+        check(lib.rl_cache_commit(self.h), "rl_cache_commit")
+
+    def abort(self):
+        check(lib.rl_cache_abort(self.h), "rl_cache_abort")
+
+    def generation(self, slot: int) -> int:
+        return lib.rl_cache_generation(self.h, slot)
+
+    def table(self):
+        import numpy as np
+        t = np.empty((self.n_layers, self.n_experts), np.int32)
+        check(lib.rl_cache_table(self.h, t.ctypes.data), "rl_cache_table")
+        return t
+
+    def stats(self) -> dict:
+        import numpy as np
+        out = np.zeros(5, np.int64)
+        check(lib.rl_cache_stats(self.h, out.ctypes.data), "rl_cache_stats")
+        return dict(zip(("reservations", "hits", "misses", "evictions", "aborts"), out.tolist()))

@@ -19,6 +19,7 @@ from __future__ import annotations
 
 from typing import List, Sequence
 
+import numpy as np
 import torch
 
 from . import binding as B
@@ -91,3 +92,149 @@ class PrefillStack:
             outs.append(x[self.L])
             t0 += n
         return torch.cat(outs)
+
+
+class HostExpertStore:
+    """Every expert of a workload in host memory: the backing store misses
+    are loaded from.  ``build`` fills it from the seeded streams
+    (slot_bytes per expert, L*E experts)."""
+
+    def __init__(self, w, seed: int = 0, build: bool = True):
+        from . import synth
+        self.w = w
+        self.E = w.n_experts
+        self.slot_bytes = synth.slot_nbytes(w.hidden, w.width, w.qbits)
+        self.data = np.empty((w.n_layers * w.n_experts, self.slot_bytes), np.uint8)
+        if build:
+            for i in range(w.n_layers * w.n_experts):
+                synth.expert_slot(w, i // self.E, i % self.E, seed, out=self.data[i])
+
+    def __call__(self, layer: int, expert: int):
+        return self.data[layer * self.E + expert]
+
+
+class ServicedDecodeStack:
+    """Decode through L layers with a bounded expert pool: a layer whose
+    selection names a non-resident expert raises its flag, and every kernel
+    after it in that layer returns at once; the host then loads that layer's
+    missing experts into least recently used slots (the library's expert
+    cache), updates the device residency table, runs the layer again and
+    resumes at the next layer ("Red Lite dev23 - per-layer early-out and
+    pre-gated expert prefetch", "What changed": layers before f are
+    complete, the CPU loads only layer f's missing experts, runs them and
+    resumes at f+1).
+
+    Two paths, as in the notes' policy: the early-out path replays the whole
+    rest of the token as one HIP graph and looks at the layers' flags
+    afterwards; the synchronous path replays one layer at a time and services
+    a miss as soon as its layer shows it.  A token with more than
+    ``early_out_limit`` early-outs sends the next tokens to the synchronous
+    path; a token that needed no load sends them back ("Red Lite dev23",
+    "What changed", policy).
+
+    The layers after an early-out still run on the unfinished input; their
+    results are overwritten when the token resumes, so every layer's
+    output equals that of a fully resident stack."""
+
+    def __init__(self, model: DeviceModel, source, early_out_limit: int = 4):
+        w = model.w
+        self.model, self.source, self.limit = model, source, early_out_limit
+        self.L, self.E, self.k = w.n_layers, w.n_experts, w.top_k
+        self.stack = DecodeStack(model)
+        s = self.stack
+        # one flag word per layer in one tensor, so one copy reads them all
+        self.flags = torch.zeros(self.L, dtype=torch.int32, device=DEV)
+        for l in range(self.L):
+            s.routes[l].early_out = self.flags[l:l + 1]
+        self.table = np.array(model.table, dtype=np.int32)
+        n_slots = int(model.pool.shape[0])
+        self.cache = B.ExpertCache(n_slots, self.L, self.E)
+        for l, e in zip(*np.nonzero(self.table >= 0)):
+            self.cache.insert(int(l), int(e), int(self.table[l, e]))
+        self.stage = torch.empty(self.k, model.slot_bytes, dtype=torch.uint8, pin_memory=True)
+        self.table_h = torch.from_numpy(self.table).pin_memory()
+        self.sync_path = False
+        self.stats = dict(tokens=0, early_outs=0, loads=0, sync_tokens=0, evictions=0)
+        self.stream = torch.cuda.Stream()
+        self.suffix = [self._capture(l, self.L) for l in range(self.L)]
+        self.single = [self._capture(l, l + 1) for l in range(self.L)]
+
+    def _layer(self, l):
+        s = self.stack
+        self.model.decode(l, s.a[l], s.routes[l], s.scratch, s.y[l])
+        B.rl_residual_rmsnorm(1, s.H, s.x[l], s.y[l], s.routes[l].early_out, s.x[l + 1],
+                              s.a[l + 1], EPS)
+
+    def _capture(self, l0, l1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            for l in range(l0, l1):           # warm once outside the capture
+                self._layer(l)
+            with torch.cuda.graph(g, stream=self.stream):
+                for l in range(l0, l1):
+                    self._layer(l)
+        return g
+
+    def _service(self, f):
+        """Load layer f's missing experts, then run layer f again."""
+        s = self.stack
+        ids = s.routes[f].ids[0].cpu().numpy()
+        n, slots, load, evicted, gens = self.cache.reserve(f, ids)
+        pool = self.model.pool
+        for i in np.nonzero(load)[0] if n else ():
+            self.stage[i].numpy()[:] = self.source(f, int(ids[i]))
+            pool[int(slots[i])].copy_(self.stage[i], non_blocking=True)
+            self.table[f, ids[i]] = slots[i]
+            if evicted[i] >= 0:
+                self.table[evicted[i] // self.E, evicted[i] % self.E] = -1
+                self.stats["evictions"] += 1
+        if n:
+            self.table_h.numpy()[:] = self.table
+            self.model.residency.copy_(self.table_h, non_blocking=True)
+        self.cache.commit()
+        self.stats["loads"] += n
+        self.single[f].replay()
+        flag = int(self.flags[f].item())
+        assert flag == 0, f"layer {f} still misses after its experts were loaded"
+        for sl, g in zip(slots, gens):        # no slot of the run was reloaded meanwhile
+            assert self.cache.generation(int(sl)) == int(g)
+
+    def token(self, x0: torch.Tensor) -> torch.Tensor:
+        s = self.stack
+        with torch.cuda.stream(self.stream):
+            s.x[0].copy_(x0.reshape(s.H))
+            B.rl_rmsnorm(1, s.H, s.x[0], s.a[0], EPS)
+            n_eo, l = 0, 0
+            sync = self.sync_path
+            while l < self.L:
+                if not sync:
+                    self.suffix[l].replay()
+                    flags = self.flags.cpu().numpy()
+                    hit = np.nonzero(flags[l:])[0]
+                    if hit.size == 0:
+                        break
+                    f = l + int(hit[0])
+                else:
+                    self.single[l].replay()
+                    if int(self.flags[l].item()) == 0:
+                        l += 1
+                        continue
+                    f = l
+                n_eo += 1
+                self._service(f)
+                l = f + 1
+            # the experts every layer used become the most recently used
+            # ("Red Lite dev21", "What changed": LRU stamps refreshed after
+            # the token); a later layer's loads may have evicted some
+            ids = torch.stack([r.ids[0] for r in s.routes]).cpu().numpy()
+            for layer in range(self.L):
+                self.cache.touch(layer, ids[layer])
+            self.stream.synchronize()
+        self.stats["tokens"] += 1
+        self.stats["early_outs"] += n_eo
+        self.stats["sync_tokens"] += int(sync)
+        if n_eo > self.limit:
+            self.sync_path = True
+        elif n_eo == 0:
+            self.sync_path = False
+        return s.x[self.L]

@@ -141,12 +141,22 @@ def residency(w: Workload, seed: int = 0) -> np.ndarray:
     All-resident workloads place the L*E experts at a random permutation of
     the slots.  A workload with ``resident`` = R picks R (layer, expert)
     entries uniformly without replacement and gives them a random permutation
-    of slots 0..R-1.
+    of slots 0..R-1; with ``popular`` it picks each layer's R/L most popular
+    experts instead (lowest Zipf rank, the ranks ``router_bias`` uses).
     """
     rng = _rng(seed, w.wid, K_RESIDENCY)
     n = w.n_layers * w.n_experts
     if w.resident < 0:
         table = rng.permutation(n).astype(np.int32)
+    elif w.popular:
+        per = w.resident // w.n_layers
+        chosen = []
+        for layer in range(w.n_layers):
+            rank = _rng(seed, w.wid, K_BIAS, layer).permutation(w.n_experts) + 1
+            chosen.append(layer * w.n_experts + np.nonzero(rank <= per)[0])
+        chosen = np.concatenate(chosen)
+        table = np.full(n, -1, np.int32)
+        table[chosen] = rng.permutation(chosen.size).astype(np.int32)
     else:
         table = np.full(n, -1, np.int32)
         chosen = rng.choice(n, size=w.resident, replace=False)

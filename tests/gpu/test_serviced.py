@@ -1,0 +1,55 @@
+"""Decode with a bounded expert pool and miss service ("Red Lite dev23 -
+per-layer early-out and pre-gated expert prefetch", "What changed": a
+layer that selects a non-resident expert stops the token there; the host
+loads that layer's missing experts, runs it and resumes at the next layer).
+
+A small stack whose pool holds only each layer's most popular experts is
+driven token by token through ServicedDecodeStack; the same tokens through
+an all-resident stack of the same weights give every layer's input, and
+the serviced stack must reproduce them bit for bit (same kernels, same
+inputs once every selected expert is loaded).  Both policy paths are
+exercised: the early-out path (whole rest of the token as one graph) and
+the synchronous path that follows a token with many early-outs."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_routed_expert_rl_amd import synth
+from quantized_routed_expert_rl_amd.device import DeviceModel, to_dev
+from quantized_routed_expert_rl_amd.stack import DecodeStack, HostExpertStore, ServicedDecodeStack
+from quantized_routed_expert_rl_amd.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _workloads(per_layer):
+    hot = Workload("serviced", 9, 256, 32, 4, 256, 6, 10, zipf=True, resident=6 * per_layer,
+                   popular=True)
+    full = Workload(**{**hot.__dict__, "resident": -1, "popular": False})
+    return hot, full
+
+
+@pytest.mark.parametrize("per_layer,limit", [(8, 4), (8, 0), (16, 4)])
+def test_serviced_stack_equals_resident_stack(per_layer, limit):
+    hot, full = _workloads(per_layer)
+    xs = synth.activations(hot, hot.tokens)
+    ref = DecodeStack(DeviceModel(full))
+    want = []
+    for t in range(hot.tokens):
+        ref.token(to_dev(xs[t]))
+        torch.cuda.synchronize()
+        want.append(ref.x.cpu().numpy().copy())
+    svc = ServicedDecodeStack(DeviceModel(hot), HostExpertStore(hot), early_out_limit=limit)
+    for t in range(hot.tokens):
+        svc.token(to_dev(xs[t]))
+        torch.cuda.synchronize()
+        got = svc.stack.x.cpu().numpy()
+        for l in range(hot.n_layers + 1):
+            assert np.array_equal(got[l], want[t][l]), f"token {t} layer {l}"
+    st = svc.stats
+    print(st, svc.cache.stats())
+    assert st["loads"] > 0 and st["early_outs"] > 0 and st["evictions"] > 0
+    if limit == 0:
+        assert st["sync_tokens"] > 0
+    # the device table always mirrors the cache
+    assert np.array_equal(svc.model.residency.cpu().numpy(), svc.cache.table())
