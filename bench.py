@@ -400,6 +400,40 @@ def main():
                             f"Zipf-biased routing, all experts resident, {qb}-bit block weights"}
             del mp_, ps
             torch.cuda.empty_cache()
+        # decode with a bounded pool (each layer's 224 most popular experts
+        # resident) and miss service, without and with the pre-gated prefetch
+        from quantized_routed_expert_rl_amd.stack import HostExpertStore, ServicedDecodeStack
+        wh = workloads.get("decode_48l_hot")
+        store = HostExpertStore(wh)
+        Xh = to_dev(synth.activations(wh, wh.tokens))
+        for pf in (False, True):
+            mh = DeviceModel(wh, pool=store.device_pool(synth.residency(wh)))
+            sv = ServicedDecodeStack(mh, store, prefetch=pf)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(wh.tokens):
+                sv.token(Xh[t])
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            st = sv.stats
+            n = st["tokens"]
+            stacks["decode_48l_hot" + ("_prefetch" if pf else "")] = {
+                "tokens_per_s": round(n / dt, 1), "ms_per_token": round(dt * 1e3 / n, 3),
+                "early_outs_per_token": round(st["early_outs"] / n, 2),
+                "critical_loads_per_token": round(st["loads"] / n, 2),
+                "prefetch_loads_per_token": round(st["prefetch_loads"] / n, 2),
+                "run_time_hit_rate": round(1 - st["loads"] / (n * wh.n_layers * wh.top_k), 4),
+                "prediction_precision": (round(st["predicted_selected"]
+                                               / (st["predictions"] * wh.top_k), 4)
+                                         if st["predictions"] else None),
+                "synchronous_tokens": st["sync_tokens"],
+                "workload": f"{wh.tokens} sequential tokens through 48 decode layers, Zipf-biased "
+                            "routing, 10752 slots seeded with each layer's 224 most popular experts, "
+                            "misses loaded from host memory into least recently used slots"
+                            + ("; next layer's experts predicted and prefetched" if pf else "")}
+            del sv, mh
+            torch.cuda.empty_cache()
+        del store
         line["stacks"] = stacks
 
     # -------------------------------------------------------- cpu oracle

@@ -94,23 +94,52 @@ class PrefillStack:
         return torch.cat(outs)
 
 
+class _nullcontext:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
 class HostExpertStore:
-    """Every expert of a workload in host memory: the backing store misses
-    are loaded from.  ``build`` fills it from the seeded streams
-    (slot_bytes per expert, L*E experts)."""
+    """Every expert of a workload in pinned host memory: the backing store
+    misses are loaded from, copied straight into pool slots.  ``build``
+    fills it from the seeded streams (slot_bytes per expert, L*E experts)."""
 
     def __init__(self, w, seed: int = 0, build: bool = True):
         from . import synth
         self.w = w
         self.E = w.n_experts
         self.slot_bytes = synth.slot_nbytes(w.hidden, w.width, w.qbits)
-        self.data = np.empty((w.n_layers * w.n_experts, self.slot_bytes), np.uint8)
+        self.tensor = torch.empty(w.n_layers * w.n_experts, self.slot_bytes, dtype=torch.uint8,
+                                  pin_memory=True)
+        self.data = self.tensor.numpy()
         if build:
             for i in range(w.n_layers * w.n_experts):
                 synth.expert_slot(w, i // self.E, i % self.E, seed, out=self.data[i])
 
     def __call__(self, layer: int, expert: int):
         return self.data[layer * self.E + expert]
+
+    def row(self, layer: int, expert: int) -> torch.Tensor:
+        return self.tensor[layer * self.E + expert]
+
+    def device_pool(self, table, step: int = 256) -> torch.Tensor:
+        """A device slot pool holding, for every resident entry of ``table``,
+        that expert's bytes (the pool a cache seeded from the table needs)."""
+        n_slots = int(table.max()) + 1
+        pool = torch.empty(n_slots, self.slot_bytes, dtype=torch.uint8, device=DEV)
+        key_of_slot = np.full(n_slots, -1, np.int64)
+        held = np.nonzero(table.ravel() >= 0)[0]
+        key_of_slot[table.ravel()[held]] = held
+        stage = torch.empty(step, self.slot_bytes, dtype=torch.uint8, pin_memory=True)
+        for s0 in range(0, n_slots, step):
+            keys = key_of_slot[s0:s0 + step]
+            n = keys.size
+            stage.numpy()[:n] = self.data[np.maximum(keys, 0)]
+            pool[s0:s0 + n].copy_(stage[:n])
+        return pool
 
 
 class ServicedDecodeStack:
@@ -134,9 +163,20 @@ class ServicedDecodeStack:
 
     The layers after an early-out still run on the unfinished input; their
     results are overwritten when the token resumes, so every layer's
-    output equals that of a fully resident stack."""
+    output equals that of a fully resident stack.
 
-    def __init__(self, model: DeviceModel, source, early_out_limit: int = 4):
+    ``prefetch`` adds the notes' pre-gated prefetch to the synchronous path
+    ("Red Lite dev23", "What changed", pre-gated prefetch): layer l+1's router
+    applied to layer l's input predicts layer l+1's selection (rl_route into
+    buffers of its own, in layer l's graph, so no layer flag is touched);
+    after layer l the host reserves the predicted experts in the cache and
+    queues their copies ahead of layer l+1, which then finds most of its
+    misses resident.
+    ``stats`` counts the predictions and how many predicted experts layer
+    l+1 then selected (the accuracy the notes did not measure)."""
+
+    def __init__(self, model: DeviceModel, source, early_out_limit: int = 4,
+                 prefetch: bool = False):
         w = model.w
         self.model, self.source, self.limit = model, source, early_out_limit
         self.L, self.E, self.k = w.n_layers, w.n_experts, w.top_k
@@ -152,12 +192,27 @@ class ServicedDecodeStack:
         for l, e in zip(*np.nonzero(self.table >= 0)):
             self.cache.insert(int(l), int(e), int(self.table[l, e]))
         self.stage = torch.empty(self.k, model.slot_bytes, dtype=torch.uint8, pin_memory=True)
+        self.pstage = torch.empty(self.k, model.slot_bytes, dtype=torch.uint8, pin_memory=True)
         self.table_h = torch.from_numpy(self.table).pin_memory()
         self.sync_path = False
-        self.stats = dict(tokens=0, early_outs=0, loads=0, sync_tokens=0, evictions=0)
+        self.prefetch = prefetch
+        self.stats = dict(tokens=0, early_outs=0, loads=0, sync_tokens=0, evictions=0,
+                          predictions=0, predicted_selected=0, prefetch_loads=0)
+        self.pred = RouteBuffers.alloc(1, self.k, self.E, with_logits=False)
+        self.pred_scratch = torch.zeros(B.rl_route_scratch_bytes(model.desc, 1),
+                                        dtype=torch.uint8, device=DEV)
+        self.h_flags = torch.empty(self.L, dtype=torch.int32, pin_memory=True)
+        self.h_pred = torch.empty(self.k, dtype=torch.int32, pin_memory=True)
         self.stream = torch.cuda.Stream()
         self.suffix = [self._capture(l, self.L) for l in range(self.L)]
         self.single = [self._capture(l, l + 1) for l in range(self.L)]
+        # layer l with the prediction of layer l+1's selection in the same graph
+        self.single_pf = ([self._capture(l, l + 1, predict=True) for l in range(self.L - 1)]
+                          if prefetch else [])
+
+    def _predict(self, l):
+        """Layer l+1's router on layer l's input, into the prediction buffers."""
+        self.model.route(l + 1, self.stack.a[l:l + 1], self.pred, self.pred_scratch)
 
     def _layer(self, l):
         s = self.stack
@@ -165,26 +220,30 @@ class ServicedDecodeStack:
         B.rl_residual_rmsnorm(1, s.H, s.x[l], s.y[l], s.routes[l].early_out, s.x[l + 1],
                               s.a[l + 1], EPS)
 
-    def _capture(self, l0, l1):
+    def _capture(self, l0, l1, predict=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(self.stream):
-            for l in range(l0, l1):           # warm once outside the capture
-                self._layer(l)
-            with torch.cuda.graph(g, stream=self.stream):
-                for l in range(l0, l1):
-                    self._layer(l)
+            for rep in range(2):              # once to warm up, once captured
+                with (torch.cuda.graph(g, stream=self.stream) if rep else _nullcontext()):
+                    if predict:
+                        self._predict(l0)
+                    for l in range(l0, l1):
+                        self._layer(l)
         return g
 
-    def _service(self, f):
-        """Load layer f's missing experts, then run layer f again."""
-        s = self.stack
-        ids = s.routes[f].ids[0].cpu().numpy()
-        n, slots, load, evicted, gens = self.cache.reserve(f, ids)
+    def _load(self, layer, ids, stage):
+        """Reserve layer's ids in the cache and queue the copies of the
+        missing ones (from the pinned rows ``stage``) and the table update on
+        the stream; returns (loads, slots, gens)."""
+        n, slots, load, evicted, gens = self.cache.reserve(layer, ids)
         pool = self.model.pool
         for i in np.nonzero(load)[0] if n else ():
-            self.stage[i].numpy()[:] = self.source(f, int(ids[i]))
-            pool[int(slots[i])].copy_(self.stage[i], non_blocking=True)
-            self.table[f, ids[i]] = slots[i]
+            if hasattr(self.source, "row"):      # pinned store: one copy, host to slot
+                pool[int(slots[i])].copy_(self.source.row(layer, int(ids[i])), non_blocking=True)
+            else:
+                stage[i].numpy()[:] = self.source(layer, int(ids[i]))
+                pool[int(slots[i])].copy_(stage[i], non_blocking=True)
+            self.table[layer, ids[i]] = slots[i]
             if evicted[i] >= 0:
                 self.table[evicted[i] // self.E, evicted[i] % self.E] = -1
                 self.stats["evictions"] += 1
@@ -192,6 +251,13 @@ class ServicedDecodeStack:
             self.table_h.numpy()[:] = self.table
             self.model.residency.copy_(self.table_h, non_blocking=True)
         self.cache.commit()
+        return n, slots, gens
+
+    def _service(self, f):
+        """Load layer f's missing experts, then run layer f again."""
+        s = self.stack
+        ids = s.routes[f].ids[0].cpu().numpy()
+        n, slots, gens = self._load(f, ids, self.stage)
         self.stats["loads"] += n
         self.single[f].replay()
         flag = int(self.flags[f].item())
@@ -206,6 +272,7 @@ class ServicedDecodeStack:
             B.rl_rmsnorm(1, s.H, s.x[0], s.a[0], EPS)
             n_eo, l = 0, 0
             sync = self.sync_path
+            predicted = {}
             while l < self.L:
                 if not sync:
                     self.suffix[l].replay()
@@ -215,11 +282,22 @@ class ServicedDecodeStack:
                         break
                     f = l + int(hit[0])
                 else:
-                    self.single[l].replay()
-                    if int(self.flags[l].item()) == 0:
-                        l += 1
-                        continue
-                    f = l
+                    predict = self.prefetch and l + 1 < self.L
+                    (self.single_pf if predict else self.single)[l].replay()
+                    # one wait per layer: its flag and the prediction together
+                    self.h_flags.copy_(self.flags, non_blocking=True)
+                    if predict:
+                        self.h_pred.copy_(self.pred.ids[0], non_blocking=True)
+                    self.stream.synchronize()
+                    if int(self.h_flags[l]) != 0:
+                        n_eo += 1
+                        self._service(l)
+                    if predict:                       # queued ahead of layer l+1
+                        pids = self.h_pred.numpy().copy()
+                        predicted[l + 1] = pids
+                        self.stats["prefetch_loads"] += self._load(l + 1, pids, self.pstage)[0]
+                    l += 1
+                    continue
                 n_eo += 1
                 self._service(f)
                 l = f + 1
@@ -229,6 +307,9 @@ class ServicedDecodeStack:
             ids = torch.stack([r.ids[0] for r in s.routes]).cpu().numpy()
             for layer in range(self.L):
                 self.cache.touch(layer, ids[layer])
+            for layer, pids in predicted.items():
+                self.stats["predictions"] += 1
+                self.stats["predicted_selected"] += len(set(pids.tolist()) & set(ids[layer].tolist()))
             self.stream.synchronize()
         self.stats["tokens"] += 1
         self.stats["early_outs"] += n_eo

@@ -9,7 +9,8 @@ an all-resident stack of the same weights give every layer's input, and
 the serviced stack must reproduce them bit for bit (same kernels, same
 inputs once every selected expert is loaded).  Both policy paths are
 exercised: the early-out path (whole rest of the token as one graph) and
-the synchronous path that follows a token with many early-outs."""
+the synchronous path that follows a token with many early-outs, with and
+without the pre-gated prefetch of the next layer's predicted experts."""
 import numpy as np
 import pytest
 import torch
@@ -29,8 +30,9 @@ def _workloads(per_layer):
     return hot, full
 
 
-@pytest.mark.parametrize("per_layer,limit", [(8, 4), (8, 0), (16, 4)])
-def test_serviced_stack_equals_resident_stack(per_layer, limit):
+@pytest.mark.parametrize("per_layer,limit,prefetch", [(8, 4, False), (8, 0, False),
+                                                     (16, 4, False), (8, 0, True)])
+def test_serviced_stack_equals_resident_stack(per_layer, limit, prefetch):
     hot, full = _workloads(per_layer)
     xs = synth.activations(hot, hot.tokens)
     ref = DecodeStack(DeviceModel(full))
@@ -39,7 +41,8 @@ def test_serviced_stack_equals_resident_stack(per_layer, limit):
         ref.token(to_dev(xs[t]))
         torch.cuda.synchronize()
         want.append(ref.x.cpu().numpy().copy())
-    svc = ServicedDecodeStack(DeviceModel(hot), HostExpertStore(hot), early_out_limit=limit)
+    svc = ServicedDecodeStack(DeviceModel(hot), HostExpertStore(hot), early_out_limit=limit,
+                              prefetch=prefetch)
     for t in range(hot.tokens):
         svc.token(to_dev(xs[t]))
         torch.cuda.synchronize()
@@ -51,5 +54,8 @@ def test_serviced_stack_equals_resident_stack(per_layer, limit):
     assert st["loads"] > 0 and st["early_outs"] > 0 and st["evictions"] > 0
     if limit == 0:
         assert st["sync_tokens"] > 0
+    if prefetch:
+        assert st["predictions"] > 0 and st["prefetch_loads"] > 0
+        assert 0 < st["predicted_selected"] <= st["predictions"] * hot.top_k
     # the device table always mirrors the cache
     assert np.array_equal(svc.model.residency.cpu().numpy(), svc.cache.table())
