@@ -209,11 +209,18 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
 }
 
 // ------------------------------------------------- down + ordered sum
+// Byte offset of the staged h rows in the down kernel's dynamic LDS, after
+// the digits (nw * KBD KiB), exponents (nw * KBD ints) and e (k * RPT floats),
+// rounded up to 16 bytes.
+__host__ __device__ constexpr int decode_down_hf_offset(int nw, int KBD, int k) {
+  return (nw * KBD * 1024 + nw * KBD * 4 + k * (16 / (KBD < 4 ? KBD : 4)) * 4 + 15) & ~15;
+}
+
 // Block = RPT output rows i for all k experts; one wave per expert (up to
 // the wave count; more experts loop).  A wave turns h_r into digit operands
 // in its own LDS region while its down codes load, runs NH diagonal tiles,
 // and leaves e_r[i] in LDS; then y[i] = fma(w_r, e_r[i], acc), r = 0..k-1.
-// Dynamic LDS: nw * (KBD*1024 + KBD*4) + k*RPT*4 bytes.
+// Dynamic LDS: nw * (KBD*1024 + KBD*4) + k*RPT*4 bytes, then nw staged h rows.
 template <int KBD, int QBITS>
 __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
     PoolView pv, int H, int F, int k, const int32_t* __restrict__ slots,
@@ -228,24 +235,40 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
   uint8_t* s_hq = s_dyn + wv * KBD * 1024;
   int* s_he = reinterpret_cast<int*>(s_dyn + nw * KBD * 1024) + wv * KBD;
   float* s_e = reinterpret_cast<float*>(s_dyn + nw * KBD * 1024 + nw * KBD * 4);
-  // the flag and the first expert's slot are loaded together; only the code
-  // loads (whose addresses need a valid slot) wait for the flag
+  uint8_t* s_hf = s_dyn + decode_down_hf_offset(nw, KBD, k) + wv * KBD * 1024;   // h_r (F floats)
+  // The first expert's h_r and the k slots are copied straight into LDS
+  // (global_load_lds, stores the compiler keeps in place) before the flag is
+  // looked at: all of these addresses are valid either way, so the flag's
+  // latency overlaps theirs.  Only the code loads, whose addresses need a
+  // resident slot, wait for the flag; h_r's quantisation then overlaps them
+  // (loads complete in issue order).
+  constexpr int NU = (16 * KBD + 63) / 64;   // runs of 16 values per lane
   const uint32_t flag = *early_out;
-  int slot_next = slots[wv < k ? wv : 0];
+  __shared__ int s_sl[16][64];           // each wave's copy of the k slots (k <= 32)
+  {
+    const uint8_t* g = reinterpret_cast<const uint8_t*>(hbuf + int64_t(wv < k ? wv : 0) * F) + 16 * lane;
+#pragma unroll
+    for (int c = 0; c < KBD; ++c) __builtin_amdgcn_global_load_lds(g + c * 1024, s_hf + c * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(slots + (lane < k ? lane : 0), &s_sl[wv][0], 4, 0, 0);
+  }
   if (flag) return;
   const int i0 = blockIdx.x * RPT;
   const int rho = lane & 15, q = lane >> 4;
   const int64_t blk = int64_t(i0 + rho / BPT) * KBD + rho % BPT;
-  constexpr int NU = (16 * KBD + 63) / 64;   // runs of 16 values per lane
   for (int r = wv; r < k; r += nw) {
-    // h_r first: its quantisation then overlaps the code loads (loads
-    // complete in issue order)
-    const float* hr = hbuf + int64_t(r) * F;
     float v[NU][16];
+    if (r == wv) {
+      __builtin_amdgcn_s_waitcnt(0);     // the copy into LDS has landed
+      wave_lds_sync();
+      const float* hf = reinterpret_cast<const float*>(s_hf);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) load_run(hr, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
-    const int slot = slot_next;
-    if (r + nw < k) slot_next = slots[r + nw];
+      for (int u = 0; u < NU; ++u) load_run(hf, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
+    } else {
+      const float* hr = hbuf + int64_t(r) * F;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) load_run(hr, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
+    }
+    const int slot = s_sl[wv][r];
     const uint8_t* td = tensor_base(pv, slot, 2);
     TileCodes cd[NH];
 #pragma unroll
@@ -321,7 +344,7 @@ void launch_decode_gateup_mfma(const DecodeArgs& a, hipStream_t st) {
 int decode_down_mfma_waves(int k, int F) {
   const int kbd = F / 256;
   int nw = k < 16 ? k : 16;
-  const int cap = (60 * 1024) / (kbd * 1028);
+  const int cap = (60 * 1024) / (kbd * 2052);   // digits, exponents and staged h per wave
   return nw < cap ? nw : cap;
 }
 
@@ -330,7 +353,7 @@ static void down_mfma(const DecodeArgs& a, hipStream_t st) {
   constexpr int BPT = KBD < 4 ? KBD : 4;
   constexpr int RPT = 16 / BPT;
   const int nw = decode_down_mfma_waves(a.k, a.F);
-  const size_t lds = size_t(nw) * (KBD * 1024 + KBD * 4) + size_t(a.k) * RPT * 4;
+  const size_t lds = size_t(decode_down_hf_offset(nw, KBD, a.k)) + size_t(nw) * KBD * 1024;
   decode_down_sum_mfma_kernel<KBD, QBITS><<<a.H / RPT, 64 * nw, lds, st>>>(
       a.pool, a.H, a.F, a.k, a.slots, a.weights, a.hbuf, a.early_out, a.y);
 }
