@@ -406,9 +406,13 @@ def main():
         wh = workloads.get("decode_48l_hot")
         store = HostExpertStore(wh)
         Xh = to_dev(synth.activations(wh, wh.tokens))
-        for pf in (False, True):
+        runs = [("", dict()), ("_prefetch", dict(prefetch=True)),
+                ("_early_out_path", dict(early_out_limit=1 << 30)),
+                ("_early_out_path_sticky", dict(early_out_limit=1 << 30, sticky=True))]
+        for tag, kw in runs:
             mh = DeviceModel(wh, pool=store.device_pool(synth.residency(wh)))
-            sv = ServicedDecodeStack(mh, store, prefetch=pf)
+            sv = ServicedDecodeStack(mh, store, **kw)
+            pf = kw.get("prefetch", False)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for t in range(wh.tokens):
@@ -417,7 +421,7 @@ def main():
             dt = time.perf_counter() - t0
             st = sv.stats
             n = st["tokens"]
-            stacks["decode_48l_hot" + ("_prefetch" if pf else "")] = {
+            stacks["decode_48l_hot" + tag] = {
                 "tokens_per_s": round(n / dt, 1), "ms_per_token": round(dt * 1e3 / n, 3),
                 "early_outs_per_token": round(st["early_outs"] / n, 2),
                 "critical_loads_per_token": round(st["loads"] / n, 2),
@@ -430,7 +434,9 @@ def main():
                 "workload": f"{wh.tokens} sequential tokens through 48 decode layers, Zipf-biased "
                             "routing, 10752 slots seeded with each layer's 224 most popular experts, "
                             "misses loaded from host memory into least recently used slots"
-                            + ("; next layer's experts predicted and prefetched" if pf else "")}
+                            + ("; next layer's experts predicted and prefetched" if pf else "")
+                            + ("; early-out path on every token" if "early_out_limit" in kw else "")
+                            + ("; one shared sticky flag" if kw.get("sticky") else "")}
             del sv, mh
             torch.cuda.empty_cache()
         del store

@@ -58,7 +58,18 @@ extern "C" {
 /* Shape of one MoE layer (host struct).
  * Supported: hidden in {256, 512, 1024, 2048}; width a power of two in
  * [32, 2048]; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
- * n_layers >= 1; qbits in {2, 3}; n_slots >= 0 (slots in the pool). */
+ * n_layers >= 1; qbits in {2, 3}; n_slots >= 0 (slots in the pool);
+ * flags 0 or RL_STICKY_EARLY_OUT.
+ *
+ * RL_STICKY_EARLY_OUT (decode calls only: moe_decode_layer, rl_decode_stage;
+ * rl_route, moe_prefill_chunk and rl_prefill_stage return RL_E_INVAL): the
+ * notes' single early-out flag shared by every kernel of a token ("Red Lite
+ * dev23 - per-layer early-out", "What changed": every decode kernel takes
+ * the flag and returns at once when it is set).  A call whose *early_out is
+ * already nonzero does nothing at all (no output, miss_count left as it
+ * was); a call that misses sets *early_out = 1; nothing ever clears it, so
+ * the caller zeroes it before a token (or a resumed part of one).  Without
+ * the flag bit, each call overwrites *early_out with its own miss state. */
 typedef struct rl_moe_desc {
   int32_t hidden;     /* H */
   int32_t n_experts;  /* E */
@@ -67,7 +78,10 @@ typedef struct rl_moe_desc {
   int32_t n_layers;   /* rows of the residency table */
   int32_t qbits;      /* 2 or 3 */
   int32_t n_slots;    /* slots in slot_pool; table entries >= n_slots miss */
+  int32_t flags;      /* 0 or RL_STICKY_EARLY_OUT */
 } rl_moe_desc;
+
+enum { RL_STICKY_EARLY_OUT = 1 };
 
 enum {
   RL_OK = 0,
@@ -86,7 +100,8 @@ typedef struct rl_route_out {
   float*    weights;    /* [T][k] softmax weights renormalised over the k   */
   int32_t*  slots;      /* [T][k] residency[layer][id], -1 = not resident   */
   uint32_t* miss_count; /* [1] selections with slot -1, over the T tokens  */
-  uint32_t* early_out;  /* [1] 1 when miss_count > 0, else 0 (overwritten)  */
+  uint32_t* early_out;  /* [1] 1 when miss_count > 0, else 0 (overwritten;  */
+                        /* raised only, with RL_STICKY_EARLY_OUT)          */
   float*    logits;     /* [T][E] router logits, or NULL = not stored       */
 } rl_route_out;
 

@@ -19,7 +19,7 @@ RL_OK, RL_E_INVAL, RL_E_SHAPE, RL_E_RANGE, RL_E_SCRATCH, RL_E_DEVICE = 0, -1, -2
 class RlMoeDesc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("width", C.c_int32), ("n_layers", C.c_int32), ("qbits", C.c_int32),
-                ("n_slots", C.c_int32)]
+                ("n_slots", C.c_int32), ("flags", C.c_int32)]
 
 
 class RlRouteOut(C.Structure):
@@ -124,8 +124,11 @@ def check(rc: int, what: str = "") -> int:
     return rc
 
 
-def desc(hidden, n_experts, top_k, width, n_layers=1, qbits=2, n_slots=0) -> RlMoeDesc:
-    return RlMoeDesc(hidden, n_experts, top_k, width, n_layers, qbits, n_slots)
+RL_STICKY_EARLY_OUT = 1
+
+
+def desc(hidden, n_experts, top_k, width, n_layers=1, qbits=2, n_slots=0, flags=0) -> RlMoeDesc:
+    return RlMoeDesc(hidden, n_experts, top_k, width, n_layers, qbits, n_slots, flags)
 
 
 def route_out(ids, weights, slots, miss_count, early_out, logits=None) -> RlRouteOut:

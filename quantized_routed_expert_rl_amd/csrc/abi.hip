@@ -22,6 +22,7 @@ int check_desc(const rl_moe_desc* d) {
   const bool ok_q = d->qbits == 2 || d->qbits == 3;
   if (!(ok_h && ok_f && ok_e && ok_k && ok_q && d->n_layers >= 1 && d->n_slots >= 0))
     return RL_E_SHAPE;
+  if (d->flags != 0 && d->flags != RL_STICKY_EARLY_OUT) return RL_E_INVAL;
   return RL_OK;
 }
 
@@ -155,6 +156,7 @@ DecodeArgs decode_args(const rl_moe_desc* d, int32_t layer, const float* x, cons
   da.hbuf = reinterpret_cast<float*>(s + l.hbuf);
   da.y = y;
   da.mfma = d->width % 256 == 0;
+  da.sticky = (d->flags & RL_STICKY_EARLY_OUT) != 0;
   return da;
 }
 
@@ -265,6 +267,7 @@ int rl_route(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, const float*
              const rl_route_out* out, void* scratch, int64_t scratch_bytes, void* stream) {
   int rc = check_common(d, layer, x, router_w, residency, out, scratch);
   if (rc) return rc;
+  if (d->flags & RL_STICKY_EARLY_OUT) return RL_E_INVAL;   // decode calls only
   if (n_tokens < 1) return RL_E_RANGE;
   const DecodeLayout l = decode_layout(d, n_tokens);
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
@@ -301,6 +304,7 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int
   int rc = check_common(d, layer, x, router_w, residency, route, scratch);
   if (rc) return rc;
   if (!slot_pool || !y || !aligned(slot_pool, 256) || !aligned(y, 16)) return RL_E_INVAL;
+  if (d->flags & RL_STICKY_EARLY_OUT) return RL_E_INVAL;   // decode calls only
   if (n_tokens < 1 || plan_cap < d->top_k) return RL_E_RANGE;
   const PrefillLayout l = prefill_layout(d, n_tokens);
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
@@ -345,6 +349,7 @@ int rl_prefill_stage(const rl_moe_desc* d, int32_t stage, int32_t layer, int32_t
                      int32_t plan_cap, const float* x, const int32_t* residency,
                      const void* slot_pool, const rl_route_out* route, void* scratch,
                      int64_t scratch_bytes, float* y, void* stream) {
+  if (d && (d->flags & RL_STICKY_EARLY_OUT)) return RL_E_INVAL;   // decode calls only
   int rc = check_desc(d);
   if (rc) return rc;
   rc = check_route_out(route);

@@ -46,7 +46,9 @@ __device__ inline void load_act32(const float* __restrict__ src, float* xv, floa
 template <int RPB, int NM>
 __global__ __launch_bounds__(64) void decode_router_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
-    int E, int H, int rows, float* __restrict__ logits, float* __restrict__ logits_out) {
+    int E, int H, int rows, float* __restrict__ logits, float* __restrict__ logits_out,
+    const uint32_t* __restrict__ early_out, int sticky) {
+  if (sticky && *early_out) return;
   const int lane = threadIdx.x;
   const int e0 = blockIdx.x * rows;
   float4 xv[NM];
@@ -90,7 +92,8 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
     const float* __restrict__ x, const float* __restrict__ logits,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
-    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf) {
+    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf, int sticky) {
+  if (sticky && *early_out) return;
   constexpr int RPI = 64 / LPR;     // rows per wave iteration
   constexpr int JW = 4;             // j values per wave
   constexpr int NIT = 2 * JW / RPI > 0 ? 2 * JW / RPI : 1;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_kernel(
       }
       if (lane == 0) {
         *miss_count = uint32_t(miss);
-        *early_out = miss > 0 ? 1u : 0u;
+        if (!sticky || miss > 0) *early_out = miss > 0 ? 1u : 0u;
       }
     }
   }
@@ -206,7 +209,8 @@ static void router_rpb(const DecodeArgs& a, int rows, hipStream_t st) {
 #define RL_CASE(NM)                                                                   \
   case 256 * NM:                                                                      \
     decode_router_kernel<RPB, NM><<<grid, 64, 0, st>>>(a.x, a.W, a.bias, a.E, a.H,    \
-                                                       rows, a.logits, a.logits_out); \
+                                                       rows, a.logits, a.logits_out,  \
+                                                       a.early_out, int(a.sticky));   \
     break;
     RL_CASE(1) RL_CASE(2) RL_CASE(4) RL_CASE(8)
 #undef RL_CASE
@@ -226,7 +230,7 @@ template <int N, int QBITS, int LPR>
 static void gateup_l(const DecodeArgs& a, hipStream_t st) {
   decode_topk_gateup_kernel<N, QBITS, LPR><<<a.k * (a.F / 16), 256, 0, st>>>(
       a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
-      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf);
+      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf, int(a.sticky));
 }
 
 template <int N, int QBITS>

@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
     const float* __restrict__ x, const float* __restrict__ logits,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
-    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf) {
+    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf, int sticky) {
+  if (sticky && *early_out) return;      // a set shared flag stops the whole call
   constexpr int BPT = KB < 4 ? KB : 4;   // K-blocks per tile
   constexpr int RPT = 16 / BPT;          // output rows per tile
   constexpr int NH = KB / BPT;           // tiles per tensor
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
       const int miss = finish_token(sel_ids, sel_lg, sel_res, k, E, n_slots, ids, weights, slots);
       if (lane == 0) {
         *miss_count = uint32_t(miss);
-        *early_out = miss > 0 ? 1u : 0u;
+        if (!sticky || miss > 0) *early_out = miss > 0 ? 1u : 0u;   // sticky: only raised
       }
     } else {
       const int slot = lane < k ? slot_of(sel_res[lane], n_slots) : 0;
@@ -311,7 +312,7 @@ static void gateup_mfma(const DecodeArgs& a, hipStream_t st) {
   const int blocks = a.k * (a.F / (4 * (16 / BPT))) + 1;
   decode_topk_gateup_mfma_kernel<N, KB, QBITS><<<blocks, 256, 0, st>>>(
       a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
-      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf);
+      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf, int(a.sticky));
 }
 
 template <int N, int QBITS>

@@ -41,6 +41,7 @@ struct DecodeArgs {
   float* hbuf;          // [k][F] scratch
   float* y;
   bool mfma;            // int8 matrix-core expert kernels (F % 256 == 0)
+  bool sticky;          // early_out shared and only raised: a set flag stops the call
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);

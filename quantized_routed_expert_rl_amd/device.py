@@ -91,8 +91,8 @@ class DeviceModel:
         return B.rl_route(self.desc, layer, x.shape[0], x, self.router[layer], self.bias[layer],
                           self.residency, out.c(), scratch, scratch.numel(), stream)
 
-    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None):
-        return B.moe_decode_layer(self.desc, layer, x, self.router[layer], self.bias[layer],
+    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None, desc=None):
+        return B.moe_decode_layer(desc or self.desc, layer, x, self.router[layer], self.bias[layer],
                                   self.residency, self.pool, out.c(), scratch, scratch.numel(),
                                   y, stream)
 

@@ -173,19 +173,35 @@ class ServicedDecodeStack:
     queues their copies ahead of layer l+1, which then finds most of its
     misses resident.
     ``stats`` counts the predictions and how many predicted experts layer
-    l+1 then selected (the accuracy the notes did not measure)."""
+    l+1 then selected (the accuracy the notes did not measure).
+
+    ``sticky`` gives every layer one shared early-out word in the library's
+    RL_STICKY_EARLY_OUT mode (the notes' single flag of a token): after the
+    first missing layer every kernel of the rest of the token returns at
+    once, so the early-out path wastes almost nothing; the missing layer is
+    the first whose miss count is nonzero, and the word is cleared before
+    every replay."""
 
     def __init__(self, model: DeviceModel, source, early_out_limit: int = 4,
-                 prefetch: bool = False):
+                 prefetch: bool = False, sticky: bool = False):
         w = model.w
         self.model, self.source, self.limit = model, source, early_out_limit
         self.L, self.E, self.k = w.n_layers, w.n_experts, w.top_k
         self.stack = DecodeStack(model)
         s = self.stack
-        # one flag word per layer in one tensor, so one copy reads them all
-        self.flags = torch.zeros(self.L, dtype=torch.int32, device=DEV)
+        # one flag word per layer in one tensor, so one copy reads them all;
+        # sticky: one word for every layer, and the miss counts in one tensor
+        self.sticky = sticky
+        self.flags = torch.zeros(1 if sticky else self.L, dtype=torch.int32, device=DEV)
+        self.misses = torch.zeros(self.L, dtype=torch.int32, device=DEV)
+        self.ddesc = model.desc
+        if sticky:
+            d = model.desc
+            self.ddesc = B.desc(d.hidden, d.n_experts, d.top_k, d.width, d.n_layers, d.qbits,
+                                d.n_slots, flags=B.RL_STICKY_EARLY_OUT)
         for l in range(self.L):
-            s.routes[l].early_out = self.flags[l:l + 1]
+            s.routes[l].early_out = self.flags[0:1] if sticky else self.flags[l:l + 1]
+            s.routes[l].miss_count = self.misses[l:l + 1]
         self.table = np.array(model.table, dtype=np.int32)
         n_slots = int(model.pool.shape[0])
         self.cache = B.ExpertCache(n_slots, self.L, self.E)
@@ -201,7 +217,8 @@ class ServicedDecodeStack:
         self.pred = RouteBuffers.alloc(1, self.k, self.E, with_logits=False)
         self.pred_scratch = torch.zeros(B.rl_route_scratch_bytes(model.desc, 1),
                                         dtype=torch.uint8, device=DEV)
-        self.h_flags = torch.empty(self.L, dtype=torch.int32, pin_memory=True)
+        self.h_flags = torch.empty(self.flags.numel(), dtype=torch.int32, pin_memory=True)
+        self.h_miss = torch.empty(self.L, dtype=torch.int32, pin_memory=True)
         self.h_pred = torch.empty(self.k, dtype=torch.int32, pin_memory=True)
         self.stream = torch.cuda.Stream()
         self.suffix = [self._capture(l, self.L) for l in range(self.L)]
@@ -216,7 +233,7 @@ class ServicedDecodeStack:
 
     def _layer(self, l):
         s = self.stack
-        self.model.decode(l, s.a[l], s.routes[l], s.scratch, s.y[l])
+        self.model.decode(l, s.a[l], s.routes[l], s.scratch, s.y[l], desc=self.ddesc)
         B.rl_residual_rmsnorm(1, s.H, s.x[l], s.y[l], s.routes[l].early_out, s.x[l + 1],
                               s.a[l + 1], EPS)
 
@@ -259,8 +276,10 @@ class ServicedDecodeStack:
         ids = s.routes[f].ids[0].cpu().numpy()
         n, slots, gens = self._load(f, ids, self.stage)
         self.stats["loads"] += n
+        if self.sticky:
+            self.flags.zero_()
         self.single[f].replay()
-        flag = int(self.flags[f].item())
+        flag = int(self.flags[0 if self.sticky else f].item())
         assert flag == 0, f"layer {f} still misses after its experts were loaded"
         for sl, g in zip(slots, gens):        # no slot of the run was reloaded meanwhile
             assert self.cache.generation(int(sl)) == int(g)
@@ -275,21 +294,34 @@ class ServicedDecodeStack:
             predicted = {}
             while l < self.L:
                 if not sync:
+                    if self.sticky:
+                        self.flags.zero_()
+                        self.misses[l:].zero_()
                     self.suffix[l].replay()
-                    flags = self.flags.cpu().numpy()
-                    hit = np.nonzero(flags[l:])[0]
-                    if hit.size == 0:
-                        break
-                    f = l + int(hit[0])
+                    if self.sticky:
+                        self.h_flags.copy_(self.flags, non_blocking=True)
+                        self.h_miss.copy_(self.misses, non_blocking=True)
+                        self.stream.synchronize()
+                        if int(self.h_flags[0]) == 0:
+                            break
+                        f = l + int(np.nonzero(self.h_miss.numpy()[l:])[0][0])
+                    else:
+                        flags = self.flags.cpu().numpy()
+                        hit = np.nonzero(flags[l:])[0]
+                        if hit.size == 0:
+                            break
+                        f = l + int(hit[0])
                 else:
                     predict = self.prefetch and l + 1 < self.L
+                    if self.sticky:
+                        self.flags.zero_()
                     (self.single_pf if predict else self.single)[l].replay()
                     # one wait per layer: its flag and the prediction together
                     self.h_flags.copy_(self.flags, non_blocking=True)
                     if predict:
                         self.h_pred.copy_(self.pred.ids[0], non_blocking=True)
                     self.stream.synchronize()
-                    if int(self.h_flags[l]) != 0:
+                    if int(self.h_flags[0 if self.sticky else l]) != 0:
                         n_eo += 1
                         self._service(l)
                     if predict:                       # queued ahead of layer l+1

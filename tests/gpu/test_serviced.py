@@ -10,7 +10,8 @@ the serviced stack must reproduce them bit for bit (same kernels, same
 inputs once every selected expert is loaded).  Both policy paths are
 exercised: the early-out path (whole rest of the token as one graph) and
 the synchronous path that follows a token with many early-outs, with and
-without the pre-gated prefetch of the next layer's predicted experts."""
+without the pre-gated prefetch of the next layer's predicted experts, and
+with per-layer flags or one shared sticky flag."""
 import numpy as np
 import pytest
 import torch
@@ -30,9 +31,10 @@ def _workloads(per_layer):
     return hot, full
 
 
-@pytest.mark.parametrize("per_layer,limit,prefetch", [(8, 4, False), (8, 0, False),
-                                                     (16, 4, False), (8, 0, True)])
-def test_serviced_stack_equals_resident_stack(per_layer, limit, prefetch):
+@pytest.mark.parametrize("per_layer,limit,prefetch,sticky", [
+    (8, 4, False, False), (8, 0, False, False), (16, 4, False, False), (8, 0, True, False),
+    (8, 4, False, True), (16, 4, False, True), (8, 0, True, True)])
+def test_serviced_stack_equals_resident_stack(per_layer, limit, prefetch, sticky):
     hot, full = _workloads(per_layer)
     xs = synth.activations(hot, hot.tokens)
     ref = DecodeStack(DeviceModel(full))
@@ -42,7 +44,7 @@ def test_serviced_stack_equals_resident_stack(per_layer, limit, prefetch):
         torch.cuda.synchronize()
         want.append(ref.x.cpu().numpy().copy())
     svc = ServicedDecodeStack(DeviceModel(hot), HostExpertStore(hot), early_out_limit=limit,
-                              prefetch=prefetch)
+                              prefetch=prefetch, sticky=sticky)
     for t in range(hot.tokens):
         svc.token(to_dev(xs[t]))
         torch.cuda.synchronize()

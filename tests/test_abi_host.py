@@ -93,6 +93,15 @@ def test_errors_before_any_launch():
                                      None) == B.RL_E_RANGE              # hidden > 2048
     assert B.lib.rl_residual_rmsnorm(1, 2048, 0x1000, None, None, 0x1000, 0x1000, 1e-6,
                                      None) == B.RL_E_INVAL
+    sticky = B.desc(2048, 512, 10, 512, flags=B.RL_STICKY_EARLY_OUT)
+    assert B.rl_decode_scratch_bytes(sticky) > 0
+    assert B.lib.rl_decode_scratch_bytes(C.byref(B.desc(2048, 512, 10, 512, flags=2))) == B.RL_E_INVAL
+    rs = B.rl_route_scratch_bytes(sticky, 4)
+    assert B.lib.rl_route(C.byref(sticky), 0, 4, 0x1000, 0x1000, None, 0x1000, C.byref(out),
+                          0x1000, rs, None) == B.RL_E_INVAL            # decode calls only
+    sp2 = B.rl_prefill_scratch_bytes(sticky, 64)
+    assert B.lib.moe_prefill_chunk(C.byref(sticky), 0, 64, 512, 0x1000, 0x1000, None, 0x1000,
+                                   0x1000, C.byref(out), 0x1000, sp2, 0x1000, None) == B.RL_E_INVAL
     assert B.lib.rl_stream_read(None, 1 << 20, 0x1000, None) == B.RL_E_INVAL
     assert B.lib.rl_stream_read(0x1000, 1000, 0x1000, None) == B.RL_E_RANGE   # not a multiple of 16
     assert B.lib.rl_strerror(B.RL_E_SCRATCH).decode() == "scratch buffer too small"
