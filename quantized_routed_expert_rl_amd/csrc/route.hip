@@ -54,31 +54,38 @@ __global__ __launch_bounds__(512) void route_gemm_kernel(
   const float* ga = x + int64_t(va ? tb + sr : 0) * H + k0 + sc;
   const float* gb = W + int64_t(vb ? eb + sr : 0) * H + k0 + sc;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 pa0 = va ? *reinterpret_cast<const float4*>(ga) : z4;
-  float4 pa1 = va ? *reinterpret_cast<const float4*>(ga + 4) : z4;
-  float4 pb0 = vb ? *reinterpret_cast<const float4*>(gb) : z4;
-  float4 pb1 = vb ? *reinterpret_cast<const float4*>(gb + 4) : z4;
+  // two chunks in flight in registers: a chunk's loads are issued two chunks
+  // before it is staged, since one chunk of MFMAs is shorter than a load's
+  // round trip
+  float4 pa0, pa1, pb0, pb1, qa0, qa1, qb0, qb1;
+  auto fetch = [&](int c, float4& a0, float4& a1, float4& b0, float4& b1)
+      __attribute__((always_inline)) {
+    const int off = c * 64;
+    a0 = va ? *reinterpret_cast<const float4*>(ga + off) : z4;
+    a1 = va ? *reinterpret_cast<const float4*>(ga + off + 4) : z4;
+    b0 = vb ? *reinterpret_cast<const float4*>(gb + off) : z4;
+    b1 = vb ? *reinterpret_cast<const float4*>(gb + off + 4) : z4;
+  };
+  fetch(0, pa0, pa1, pb0, pb1);
+  fetch(1, qa0, qa1, qb0, qb1);
   const int r = l & 15, kq = l >> 4;
   const int ra = (wv >> 1) * 16 + r, rb = (wv & 1) * 16 + r;   // staged rows this lane reads
   v4d acc4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc4[u] = v4d{0.0, 0.0, 0.0, 0.0};
-  for (int ch = 0; ch < nch; ++ch) {
+  // one chunk: stage its registers into LDS buffer ch&1, refill them with
+  // chunk ch+2, run its MFMAs
+  auto chunk = [&](int ch, float4& a0, float4& a1, float4& b0, float4& b1)
+      __attribute__((always_inline)) {
     const int buf = ch & 1;
     float* sa = s_a[kh][buf];
     float* sb = s_b[kh][buf];
-    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc]) = pa0;
-    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc + 4]) = pa1;
-    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc]) = pb0;
-    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc + 4]) = pb1;
+    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc]) = a0;
+    *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc + 4]) = a1;
+    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc]) = b0;
+    *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc + 4]) = b1;
     __syncthreads();
-    if (ch + 1 < nch) {
-      const int off = (ch + 1) * 64;
-      pa0 = va ? *reinterpret_cast<const float4*>(ga + off) : z4;
-      pa1 = va ? *reinterpret_cast<const float4*>(ga + off + 4) : z4;
-      pb0 = vb ? *reinterpret_cast<const float4*>(gb + off) : z4;
-      pb1 = vb ? *reinterpret_cast<const float4*>(gb + off + 4) : z4;
-    }
+    if (ch + 2 < nch) fetch(ch + 2, a0, a1, b0, b1);
     float4 av[4], bv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -97,6 +104,11 @@ __global__ __launch_bounds__(512) void route_gemm_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].w), double(bv[g].w), acc4[g], 0, 0, 0);
+  };
+  // nch = H/128 is even (H is a multiple of 256), so the register sets alternate in a fixed order
+  for (int ch = 0; ch < nch; ch += 2) {
+    chunk(ch, pa0, pa1, pb0, pb1);
+    chunk(ch + 1, qa0, qa1, qb0, qb1);
   }
   v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   if (kh == 1) s_part[wv][l] = acc;
@@ -108,7 +120,7 @@ __global__ __launch_bounds__(512) void route_gemm_kernel(
   for (int v = 0; v < 4; ++v) {
     const int t = t0 + kq + 4 * v, e = e0 + r;
     if (t < T && e < E) {
-      double sum = acc[v];
+      double sum = v == 0 ? acc.x : v == 1 ? acc.y : v == 2 ? acc.z : acc.w;
       if (bias) sum += double(bias[e]);
       const float lg = float(sum);
       logits[int64_t(t) * E + e] = lg;
