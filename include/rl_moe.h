@@ -89,7 +89,8 @@ enum {
   RL_E_SHAPE = -2,    /* unsupported layer shape in the descriptor */
   RL_E_RANGE = -3,    /* layer, n_tokens or plan_cap out of range */
   RL_E_SCRATCH = -4,  /* scratch smaller than the size query returns */
-  RL_E_DEVICE = -5    /* a kernel launch failed */
+  RL_E_DEVICE = -5,   /* a kernel launch failed */
+  RL_E_STATE = -6     /* a decode driver's token failed an internal check */
 };
 
 /* Routing results of one call (host struct of device pointers).
@@ -288,6 +289,79 @@ int rl_cache_abort(rl_cache* c);
 uint32_t rl_cache_generation(const rl_cache* c, int32_t slot);
 int rl_cache_table(const rl_cache* c, int32_t* table);
 int rl_cache_stats(const rl_cache* c, int64_t* out);
+
+/* ---------------------------------------------------------------------------
+ * Decode driver: single tokens through all n_layers layers of a model whose
+ * slot pool holds only part of its experts, with miss service and resume
+ * ("Red Lite dev23 - per-layer early-out and pre-gated expert prefetch",
+ * "What changed": the first layer f that selects a non-resident expert
+ * stops the token there; f's missing experts are loaded, f runs again and
+ * the token resumes at f + 1; a token with more than a few early-outs sends
+ * the next tokens to a layer-by-layer path, a token without loads sends them
+ * back; optionally the next layer's router on the current layer's input
+ * predicts its selection and the predicted experts are loaded ahead of it).
+ * Host code driving the library's own calls: per layer moe_decode_layer on
+ * a_l = rmsnorm(x_l), then rl_residual_rmsnorm (x_{l+1} = x_l + y_l, or x_l
+ * when the layer's flag is set), replayed as HIP graphs captured at creation.
+ * Misses are copied from the host store into the slots the cache picks
+ * (hipMemcpyAsync on the stream) and the changed residency entries follow;
+ * after a token every layer's selection is touched in the cache ("Red Lite
+ * dev21", "What changed", LRU stamps refreshed after the token).
+ *
+ * rl_driver_config (host struct; the pointers stay owned by the caller and
+ * must outlive the driver):
+ *   desc             layer shape, n_layers >= 1, top_k <= 32; flags may hold
+ *                    RL_STICKY_EARLY_OUT (one shared flag word per token)
+ *   router_w         [n_layers] device pointers, each [E x H] float32
+ *   router_bias      [n_layers] device pointers ([E] float32) or NULL entries;
+ *                    NULL = no bias anywhere
+ *   residency        device [n_layers x E] int32; overwritten at creation with
+ *                    the cache's table and kept equal to it afterwards
+ *   slot_pool        device pool of desc->n_slots slots (rl_slot_bytes each)
+ *   host_store       pinned host memory (hipHostMalloc or equivalent) holding
+ *                    every expert: row layer * E + expert, rl_slot_bytes each
+ *   cache            an rl_cache over the same slots, seeded with the pool's
+ *                    resident experts; the driver reserves, commits and
+ *                    touches it and no one else may use it meanwhile
+ *   x                device [(n_layers + 1) x H] float32: after a token, x[l]
+ *                    is layer l's input and x[n_layers] the output
+ *   early_out_limit  >= 0: a token with more early-outs than this sends the
+ *                    next tokens to the layer-by-layer path
+ *   prefetch         nonzero: predict and load the next layer's experts on
+ *                    the layer-by-layer path
+ *   eps              RMSNorm epsilon
+ * rl_driver_create: allocates its device and pinned buffers, captures its
+ *   graphs on `stream` (a hipStream_t) and runs one layer eagerly; NULL on a
+ *   bad argument or a failed allocation, capture or launch.  All later
+ *   calls use the same stream.
+ * rl_driver_token: x0 device [H] float32; runs the token and returns after
+ *   the stream has drained.  RL_E_RANGE if the cache cannot hold one layer's
+ *   selection, RL_E_DEVICE on a failed launch or copy, RL_E_STATE if a
+ *   serviced layer still missed or one of its slots was reloaded meanwhile.
+ *   After any error the driver refuses further tokens (RL_E_STATE).
+ * rl_driver_stats: out[8] = tokens, early-outs, loads on the critical path,
+ *   tokens on the layer-by-layer path, evictions, predictions, predicted
+ *   experts that the layer then selected, prefetched loads.
+ * rl_driver_destroy: waits for the stream and frees the driver. */
+typedef struct rl_driver_config {
+  const rl_moe_desc* desc;
+  const float* const* router_w;
+  const float* const* router_bias;
+  int32_t* residency;
+  void* slot_pool;
+  const void* host_store;
+  rl_cache* cache;
+  float* x;
+  int32_t early_out_limit;
+  int32_t prefetch;
+  float eps;
+} rl_driver_config;
+
+typedef struct rl_decode_driver rl_decode_driver;
+rl_decode_driver* rl_driver_create(const rl_driver_config* config, void* stream);
+int rl_driver_token(rl_decode_driver* driver, const float* x0);
+int rl_driver_stats(const rl_decode_driver* driver, int64_t* out);
+void rl_driver_destroy(rl_decode_driver* driver);
 
 /* Measurement helper (not part of the MoE layer): reads `bytes` bytes of the
  * device buffer `buf` once, in 16-byte words, with a grid of eight blocks

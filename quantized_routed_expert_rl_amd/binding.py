@@ -27,6 +27,14 @@ class RlRouteOut(C.Structure):
                 ("miss_count", C.c_void_p), ("early_out", C.c_void_p), ("logits", C.c_void_p)]
 
 
+class RlDriverConfig(C.Structure):
+    _fields_ = [("desc", C.POINTER(RlMoeDesc)), ("router_w", C.POINTER(C.c_void_p)),
+                ("router_bias", C.POINTER(C.c_void_p)), ("residency", C.c_void_p),
+                ("slot_pool", C.c_void_p), ("host_store", C.c_void_p), ("cache", C.c_void_p),
+                ("x", C.c_void_p), ("early_out_limit", C.c_int32), ("prefetch", C.c_int32),
+                ("eps", C.c_float)]
+
+
 class RlPrefillLayout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("n_groups", "group_bounds", "n_buckets",
                                           "group_bucket_start", "bucket_expert",
@@ -80,6 +88,10 @@ _SIGS = {
     "rl_cache_generation": (C.c_uint32, [C.c_void_p, C.c_int32]),
     "rl_cache_table": (C.c_int, [C.c_void_p, C.c_void_p]),
     "rl_cache_stats": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "rl_driver_create": (C.c_void_p, [C.POINTER(RlDriverConfig), C.c_void_p]),
+    "rl_driver_token": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "rl_driver_stats": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "rl_driver_destroy": (None, [C.c_void_p]),
 }
 
 
@@ -292,3 +304,50 @@ class ExpertCache:
         out = np.zeros(5, np.int64)
         check(lib.rl_cache_stats(self.h, out.ctypes.data), "rl_cache_stats")
         return dict(zip(("reservations", "hits", "misses", "evictions", "aborts"), out.tolist()))
+
+
+DRIVER_STATS = ("tokens", "early_outs", "loads", "sync_tokens", "evictions", "predictions",
+                "predicted_selected", "prefetch_loads")
+
+
+class DecodeDriver:
+    """The library's decode driver (rl_driver_*): argument marshalling only.
+    ``router_w`` and ``router_bias`` are per-layer device tensors (bias
+    entries may be None), ``x`` the [(L+1) x H] device tensor the driver
+    writes every layer's input into; every object passed in must outlive the
+    driver."""
+
+    def __init__(self, d: RlMoeDesc, router_w, router_bias, residency, pool, host_store,
+                 cache: ExpertCache, x, early_out_limit: int = 4, prefetch: bool = False,
+                 eps: float = 1e-6, stream=None):
+        L = d.n_layers
+        self._keep = (d, router_w, router_bias, residency, pool, host_store, cache, x)
+        self._w = (C.c_void_p * L)(*[_ptr(t) for t in router_w])
+        self._b = None
+        if any(b is not None for b in router_bias):
+            self._b = (C.c_void_p * L)(*[_ptr(b) for b in router_bias])
+        self._desc = d
+        cfg = RlDriverConfig(C.pointer(self._desc), self._w, self._b, _ptr(residency), _ptr(pool),
+                             _ptr(host_store), cache.h, _ptr(x), early_out_limit,
+                             1 if prefetch else 0, eps)
+        self._stream = _stream(stream)
+        self.h = lib.rl_driver_create(C.byref(cfg), self._stream)
+        if not self.h:
+            raise RlError("rl_driver_create failed")
+
+    def token(self, x0):
+        check(lib.rl_driver_token(self.h, _ptr(x0)), "rl_driver_token")
+
+    def stats(self) -> dict:
+        import numpy as np
+        out = np.zeros(8, np.int64)
+        check(lib.rl_driver_stats(self.h, out.ctypes.data), "rl_driver_stats")
+        return dict(zip(DRIVER_STATS, out.tolist()))
+
+    def close(self):
+        if self.h:
+            lib.rl_driver_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()

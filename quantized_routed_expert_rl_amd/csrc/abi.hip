@@ -258,6 +258,7 @@ const char* rl_strerror(int code) {
     case RL_E_RANGE: return "layer, token count or plan cap out of range";
     case RL_E_SCRATCH: return "scratch buffer too small";
     case RL_E_DEVICE: return "kernel launch failed";
+    case RL_E_STATE: return "decode driver check failed";
     default: return "unknown error";
   }
 }

@@ -1,0 +1,448 @@
+// Host-side decode driver: one token at a time through L MoE layers whose
+// expert pool holds only part of the experts (host code; the kernels are the
+// library's own decode, route and norm launches, replayed as HIP graphs).
+//
+// Per token ("Red Lite dev23 - per-layer early-out and pre-gated expert
+// prefetch", "What changed"):
+//  - a layer whose selection names a non-resident expert raises its flag and
+//    every later kernel of that layer returns at once; the layers before the
+//    first flagged layer f are complete;
+//  - the host loads f's missing experts into slots the expert cache picks
+//    (least recently used, hits reserved first: "Red Lite dev20", LRU fix),
+//    mirrors the cache's table into the device residency table, runs layer f
+//    again and resumes at f + 1;
+//  - policy: on the early-out path the rest of the token is one graph
+//    launch and the flags are read afterwards; a token with more than
+//    `early_out_limit` early-outs sends the following tokens to the
+//    synchronous path (one launch and one wait per layer, a miss serviced as
+//    soon as its layer shows it), and a token that needed no load sends them
+//    back;
+//  - pre-gated prefetch (synchronous path, optional): layer l+1's router on
+//    layer l's input, in layer l's graph, predicts l+1's selection, and the
+//    predicted experts are reserved and copied ahead of layer l+1;
+//  - after the token every layer's selection becomes the most recently used
+//    ("Red Lite dev21 - GPU-routed decode", "What changed": LRU stamps
+//    refreshed after the token).
+// The layers after an early-out run on an unfinished input; their results are
+// overwritten when the token resumes, so every layer's output equals that of a
+// fully resident stack.
+//
+// Graphs (captured once at creation): suffix[l] = layers l .. L-1, single[l]
+// = layer l, single_pf[l] = the prediction for l+1 and layer l.  Each ends by
+// copying the flags, miss counts, selected ids (and predicted ids) into pinned
+// host mirrors, so one wait after a launch gives the host all it reads.
+// A layer = moe_decode_layer(a_l) -> y_l, then rl_residual_rmsnorm(x_l, y_l,
+// flag) -> x_{l+1}, a_{l+1}; the token starts with x_0 = x0, a_0 = rmsnorm(x0).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "rl_kernels.h"
+#include "rl_moe.h"
+
+struct rl_decode_driver {
+  rl_moe_desc d;          // as given (flags may hold RL_STICKY_EARLY_OUT)
+  rl_moe_desc dr;         // without flags: the prediction's rl_route
+  int L = 0, E = 0, H = 0, k = 0;
+  bool sticky = false, prefetch = false, sync_path = false;
+  int limit = 0;
+  float eps = 0.f;
+  hipStream_t st = nullptr;
+  std::vector<const float*> W, bias;
+  int32_t* residency = nullptr;
+  uint8_t* pool = nullptr;
+  const uint8_t* store = nullptr;
+  int64_t slot_bytes = 0;
+  rl_cache* cache = nullptr;
+  float* x = nullptr;     // caller's [(L+1) x H]
+  // device buffers (one allocation)
+  void* dev = nullptr;
+  float *a = nullptr, *y = nullptr;
+  int32_t *ids = nullptr, *slots = nullptr, *pids = nullptr, *pslots = nullptr;
+  float *wts = nullptr, *pw = nullptr;
+  uint32_t *miss = nullptr, *flags = nullptr, *pmiss = nullptr, *pflag = nullptr;
+  uint8_t *scratch = nullptr, *pscratch = nullptr;
+  int64_t scratch_bytes = 0, pscratch_bytes = 0;
+  // pinned host mirrors and the host copy of the residency table
+  void* host = nullptr;
+  uint32_t *h_flags = nullptr, *h_miss = nullptr;
+  int32_t *h_ids = nullptr, *h_pids = nullptr, *h_table = nullptr;
+  int32_t *h_pairs = nullptr, *d_pairs = nullptr;   // changed table entries (key, slot)
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> suffix, single, single_pf;
+  // tokens, early_outs, loads, sync_tokens, evictions, predictions,
+  // predicted_selected, prefetch_loads
+  int64_t stats[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool broken = false;
+};
+
+namespace {
+
+int nflags(const rl_decode_driver* v) { return v->sticky ? 1 : v->L; }
+
+rl_route_out layer_route(const rl_decode_driver* v, int l) {
+  rl_route_out o;
+  o.ids = v->ids + l * v->k;
+  o.weights = v->wts + l * v->k;
+  o.slots = v->slots + l * v->k;
+  o.miss_count = v->miss + l;
+  o.early_out = v->flags + (v->sticky ? 0 : l);
+  o.logits = nullptr;
+  return o;
+}
+
+int run_layer(rl_decode_driver* v, int l) {
+  const rl_route_out o = layer_route(v, l);
+  int rc = moe_decode_layer(&v->d, l, v->a + int64_t(l) * v->H, v->W[l], v->bias[l], v->residency,
+                            v->pool, &o, v->scratch, v->scratch_bytes, v->y + int64_t(l) * v->H,
+                            v->st);
+  if (rc) return rc;
+  return rl_residual_rmsnorm(1, v->H, v->x + int64_t(l) * v->H, v->y + int64_t(l) * v->H,
+                             o.early_out, v->x + int64_t(l + 1) * v->H,
+                             v->a + int64_t(l + 1) * v->H, v->eps, v->st);
+}
+
+// layer l+1's router on layer l's input, into the prediction buffers
+int run_predict(rl_decode_driver* v, int l) {
+  rl_route_out o;
+  o.ids = v->pids;
+  o.weights = v->pw;
+  o.slots = v->pslots;
+  o.miss_count = v->pmiss;
+  o.early_out = v->pflag;
+  o.logits = nullptr;
+  return rl_route(&v->dr, l + 1, 1, v->a + int64_t(l) * v->H, v->W[l + 1], v->bias[l + 1],
+                  v->residency, &o, v->pscratch, v->pscratch_bytes, v->st);
+}
+
+int run_mirror(rl_decode_driver* v, bool predict) {
+  hipError_t e = hipMemcpyAsync(v->h_flags, v->flags, sizeof(uint32_t) * nflags(v),
+                                hipMemcpyDeviceToHost, v->st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(v->h_miss, v->miss, sizeof(uint32_t) * v->L, hipMemcpyDeviceToHost, v->st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(v->h_ids, v->ids, sizeof(int32_t) * v->L * v->k, hipMemcpyDeviceToHost,
+                       v->st);
+  if (e == hipSuccess && predict)
+    e = hipMemcpyAsync(v->h_pids, v->pids, sizeof(int32_t) * v->k, hipMemcpyDeviceToHost, v->st);
+  return e == hipSuccess ? RL_OK : RL_E_DEVICE;
+}
+
+int run_body(rl_decode_driver* v, int l0, int l1, bool predict) {
+  int rc = predict ? run_predict(v, l0) : RL_OK;
+  for (int l = l0; l < l1 && !rc; ++l) rc = run_layer(v, l);
+  return rc ? rc : run_mirror(v, predict);
+}
+
+int capture(rl_decode_driver* v, int l0, int l1, bool predict, hipGraphExec_t* out) {
+  hipGraph_t g = nullptr;
+  if (hipStreamBeginCapture(v->st, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    return RL_E_DEVICE;
+  const int rc = run_body(v, l0, l1, predict);
+  const hipError_t e = hipStreamEndCapture(v->st, &g);
+  if (rc || e != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc ? rc : RL_E_DEVICE;
+  }
+  v->graphs.push_back(g);
+  return hipGraphInstantiate(out, g, nullptr, nullptr, 0) == hipSuccess ? RL_OK : RL_E_DEVICE;
+}
+
+int launch_wait(rl_decode_driver* v, hipGraphExec_t g) {
+  if (hipGraphLaunch(g, v->st) != hipSuccess) return RL_E_DEVICE;
+  return hipStreamSynchronize(v->st) == hipSuccess ? RL_OK : RL_E_DEVICE;
+}
+
+int clear_flags(rl_decode_driver* v, int miss_from) {
+  if (!v->sticky) return RL_OK;
+  hipError_t e = hipMemsetAsync(v->flags, 0, sizeof(uint32_t), v->st);
+  if (e == hipSuccess && miss_from < v->L)
+    e = hipMemsetAsync(v->miss + miss_from, 0, sizeof(uint32_t) * (v->L - miss_from), v->st);
+  return e == hipSuccess ? RL_OK : RL_E_DEVICE;
+}
+
+// Sends the n changed table entries staged in h_pairs to the device table
+// (one copy and one scatter launch).  The staging stays unchanged until the
+// copy has run: every path waits on the stream before the next load.
+int put_entries(rl_decode_driver* v, int n) {
+  if (n == 0) return RL_OK;
+  if (hipMemcpyAsync(v->d_pairs, v->h_pairs, sizeof(int32_t) * 2 * n, hipMemcpyHostToDevice,
+                     v->st) != hipSuccess)
+    return RL_E_DEVICE;
+  rl::launch_table_scatter(v->residency, v->d_pairs, n, v->st);
+  return hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVICE;
+}
+
+// Reserves layer's selection in the cache and queues the copies of its
+// missing experts from the host store, and the table entries that change.
+// Returns the number of loads (>= 0) or an error; slots and gens receive the
+// selection's slots and their load generations.
+int load_layer(rl_decode_driver* v, int layer, const int32_t* sel, int32_t* slots,
+               uint32_t* gens) {
+  const int k = v->k;
+  int32_t load[32], evicted[32];
+  const int n = rl_cache_reserve(v->cache, layer, sel, k, slots, load, evicted, gens);
+  if (n < 0) return n;
+  int np = 0;
+  for (int i = 0; i < k; ++i) {
+    if (!load[i]) continue;
+    const int64_t key = int64_t(layer) * v->E + sel[i];
+    if (hipMemcpyAsync(v->pool + int64_t(slots[i]) * v->slot_bytes, v->store + key * v->slot_bytes,
+                       v->slot_bytes, hipMemcpyHostToDevice, v->st) != hipSuccess) {
+      rl_cache_abort(v->cache);
+      return RL_E_DEVICE;
+    }
+    v->h_table[key] = slots[i];
+    v->h_pairs[2 * np] = int32_t(key);
+    v->h_pairs[2 * np + 1] = slots[i];
+    np += 1;
+    if (evicted[i] >= 0) {
+      v->h_table[evicted[i]] = -1;
+      v->h_pairs[2 * np] = evicted[i];
+      v->h_pairs[2 * np + 1] = -1;
+      np += 1;
+      v->stats[4] += 1;
+    }
+  }
+  const int rc = put_entries(v, np);
+  if (rc) {
+    rl_cache_abort(v->cache);
+    return rc;
+  }
+  rl_cache_commit(v->cache);
+  return n;
+}
+
+// Loads layer f's missing experts and runs layer f again; afterwards its
+// flag must be clear and no slot it used may have been reloaded.
+int service(rl_decode_driver* v, int f) {
+  int32_t sel[32], slots[32];
+  uint32_t gens[32];
+  for (int i = 0; i < v->k; ++i) sel[i] = v->h_ids[f * v->k + i];
+  const int n = load_layer(v, f, sel, slots, gens);
+  if (n < 0) return n;
+  v->stats[2] += n;
+  int rc = clear_flags(v, v->L);
+  if (!rc) rc = launch_wait(v, v->single[f]);
+  if (rc) return rc;
+  if (v->h_flags[v->sticky ? 0 : f] != 0) return RL_E_STATE;
+  for (int i = 0; i < v->k; ++i)
+    if (rl_cache_generation(v->cache, slots[i]) != gens[i]) return RL_E_STATE;
+  return RL_OK;
+}
+
+int token(rl_decode_driver* v, const float* x0) {
+  const int L = v->L, k = v->k;
+  if (hipMemcpyAsync(v->x, x0, sizeof(float) * v->H, hipMemcpyDeviceToDevice, v->st) !=
+      hipSuccess)
+    return RL_E_DEVICE;
+  int rc = rl_rmsnorm(1, v->H, v->x, v->a, v->eps, v->st);
+  if (rc) return rc;
+  const bool sync = v->sync_path;
+  int n_eo = 0, l = 0;
+  std::vector<std::pair<int, std::vector<int32_t>>> predicted;
+  while (l < L) {
+    if (!sync) {
+      if ((rc = clear_flags(v, l)) || (rc = launch_wait(v, v->suffix[l]))) return rc;
+      int f = -1;
+      if (v->sticky) {
+        if (v->h_flags[0] == 0) break;
+        for (int j = l; j < L && f < 0; ++j)
+          if (v->h_miss[j]) f = j;
+        if (f < 0) return RL_E_STATE;          // a raised flag without a miss
+      } else {
+        for (int j = l; j < L && f < 0; ++j)
+          if (v->h_flags[j]) f = j;
+        if (f < 0) break;
+      }
+      n_eo += 1;
+      if ((rc = service(v, f))) return rc;
+      l = f + 1;
+    } else {
+      const bool predict = v->prefetch && l + 1 < L;
+      if ((rc = clear_flags(v, L)) ||
+          (rc = launch_wait(v, predict ? v->single_pf[l] : v->single[l])))
+        return rc;
+      if (v->h_flags[v->sticky ? 0 : l] != 0) {
+        n_eo += 1;
+        if ((rc = service(v, l))) return rc;
+      }
+      if (predict) {                           // queued ahead of layer l+1
+        std::vector<int32_t> p(v->h_pids, v->h_pids + k);
+        int32_t slots[32];
+        uint32_t gens[32];
+        const int n = load_layer(v, l + 1, p.data(), slots, gens);
+        if (n < 0) return n;
+        v->stats[7] += n;
+        predicted.emplace_back(l + 1, std::move(p));
+      }
+      l += 1;
+    }
+  }
+  // the mirror holds every layer's last selection (the last launch copied it)
+  for (int layer = 0; layer < L; ++layer) {
+    rc = rl_cache_touch(v->cache, layer, v->h_ids + layer * k, k);
+    if (rc < 0) return rc;
+  }
+  for (const auto& pr : predicted) {
+    v->stats[5] += 1;
+    const int32_t* got = v->h_ids + pr.first * k;
+    for (int i = 0; i < k; ++i) {
+      bool dup = false;                        // count each predicted expert once
+      for (int j = 0; j < i && !dup; ++j) dup = pr.second[j] == pr.second[i];
+      if (dup) continue;
+      if (std::find(got, got + k, pr.second[i]) != got + k) v->stats[6] += 1;
+    }
+  }
+  v->stats[0] += 1;
+  v->stats[1] += n_eo;
+  v->stats[3] += sync ? 1 : 0;
+  if (n_eo > v->limit)
+    v->sync_path = true;
+  else if (n_eo == 0)
+    v->sync_path = false;
+  return RL_OK;
+}
+
+void release(rl_decode_driver* v) {
+  for (auto g : v->suffix)
+    if (g) (void)hipGraphExecDestroy(g);
+  for (auto g : v->single)
+    if (g) (void)hipGraphExecDestroy(g);
+  for (auto g : v->single_pf)
+    if (g) (void)hipGraphExecDestroy(g);
+  for (auto g : v->graphs) (void)hipGraphDestroy(g);
+  if (v->dev) (void)hipFree(v->dev);
+  if (v->host) (void)hipHostFree(v->host);
+  delete v;
+}
+
+}  // namespace
+
+extern "C" {
+
+rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
+  if (!c || !c->desc || !c->router_w || !c->residency || !c->slot_pool || !c->host_store ||
+      !c->cache || !c->x)
+    return nullptr;
+  const rl_moe_desc* d = c->desc;
+  if (rl_decode_scratch_bytes(d) < 0 || d->top_k > 32 || c->early_out_limit < 0) return nullptr;
+  const int L = d->n_layers;
+  for (int l = 0; l < L; ++l)
+    if (!c->router_w[l]) return nullptr;
+  rl_decode_driver* v = new (std::nothrow) rl_decode_driver;
+  if (!v) return nullptr;
+  v->d = *d;
+  v->dr = *d;
+  v->dr.flags = 0;
+  v->L = L;
+  v->E = d->n_experts;
+  v->H = d->hidden;
+  v->k = d->top_k;
+  v->sticky = (d->flags & RL_STICKY_EARLY_OUT) != 0;
+  v->prefetch = c->prefetch != 0 && L > 1;
+  v->limit = c->early_out_limit;
+  v->eps = c->eps;
+  v->st = static_cast<hipStream_t>(stream);
+  v->W.assign(c->router_w, c->router_w + L);
+  v->bias.assign(L, nullptr);
+  if (c->router_bias)
+    for (int l = 0; l < L; ++l) v->bias[l] = c->router_bias[l];
+  v->residency = c->residency;
+  v->pool = static_cast<uint8_t*>(c->slot_pool);
+  v->store = static_cast<const uint8_t*>(c->host_store);
+  v->slot_bytes = rl_slot_bytes(d);
+  v->cache = c->cache;
+  v->x = c->x;
+  const int64_t H = v->H, k = v->k;
+  v->scratch_bytes = rl_decode_scratch_bytes(d);
+  v->pscratch_bytes = rl_route_scratch_bytes(&v->dr, 1);
+  // one device allocation, every part 256-byte aligned
+  auto up = [](int64_t n) { return (n + 255) & ~int64_t(255); };
+  const int64_t o_a = 0, o_y = o_a + up(4 * (L + 1) * H), o_ids = o_y + up(4 * L * H),
+                o_slots = o_ids + up(4 * L * k), o_wts = o_slots + up(4 * L * k),
+                o_miss = o_wts + up(4 * L * k), o_flags = o_miss + up(4 * L),
+                o_pids = o_flags + up(4 * L), o_pslots = o_pids + up(4 * k),
+                o_pw = o_pslots + up(4 * k), o_pmiss = o_pw + up(4 * k), o_pflag = o_pmiss + 256,
+                o_pairs = o_pflag + 256, o_scr = o_pairs + up(4 * 4 * k),
+                o_pscr = o_scr + up(v->scratch_bytes), dev_bytes = o_pscr + up(v->pscratch_bytes);
+  const int64_t h_flags = 0, h_miss = h_flags + up(4 * L), h_ids = h_miss + up(4 * L),
+                h_pids = h_ids + up(4 * L * k), h_pairs = h_pids + up(4 * k),
+                h_table = h_pairs + up(4 * 4 * k), host_bytes = h_table + up(4 * int64_t(L) * v->E);
+  if (hipMalloc(&v->dev, dev_bytes) != hipSuccess) v->dev = nullptr;
+  if (hipHostMalloc(&v->host, host_bytes, hipHostMallocDefault) != hipSuccess) v->host = nullptr;
+  if (!v->dev || !v->host) {
+    release(v);
+    return nullptr;
+  }
+  uint8_t* b = static_cast<uint8_t*>(v->dev);
+  v->a = reinterpret_cast<float*>(b + o_a);
+  v->y = reinterpret_cast<float*>(b + o_y);
+  v->ids = reinterpret_cast<int32_t*>(b + o_ids);
+  v->slots = reinterpret_cast<int32_t*>(b + o_slots);
+  v->wts = reinterpret_cast<float*>(b + o_wts);
+  v->miss = reinterpret_cast<uint32_t*>(b + o_miss);
+  v->flags = reinterpret_cast<uint32_t*>(b + o_flags);
+  v->pids = reinterpret_cast<int32_t*>(b + o_pids);
+  v->pslots = reinterpret_cast<int32_t*>(b + o_pslots);
+  v->pw = reinterpret_cast<float*>(b + o_pw);
+  v->pmiss = reinterpret_cast<uint32_t*>(b + o_pmiss);
+  v->pflag = reinterpret_cast<uint32_t*>(b + o_pflag);
+  v->d_pairs = reinterpret_cast<int32_t*>(b + o_pairs);
+  v->scratch = b + o_scr;
+  v->pscratch = b + o_pscr;
+  uint8_t* hb = static_cast<uint8_t*>(v->host);
+  v->h_flags = reinterpret_cast<uint32_t*>(hb + h_flags);
+  v->h_miss = reinterpret_cast<uint32_t*>(hb + h_miss);
+  v->h_ids = reinterpret_cast<int32_t*>(hb + h_ids);
+  v->h_pids = reinterpret_cast<int32_t*>(hb + h_pids);
+  v->h_pairs = reinterpret_cast<int32_t*>(hb + h_pairs);
+  v->h_table = reinterpret_cast<int32_t*>(hb + h_table);
+  int rc = rl_cache_table(v->cache, v->h_table);
+  // the device table starts as the cache's table
+  if (!rc && hipMemcpyAsync(v->residency, v->h_table, 4 * int64_t(L) * v->E,
+                            hipMemcpyHostToDevice, v->st) != hipSuccess)
+    rc = RL_E_DEVICE;
+  if (!rc && hipMemsetAsync(v->dev, 0, dev_bytes, v->st) != hipSuccess) rc = RL_E_DEVICE;
+  // one eager layer (and prediction) before any capture
+  if (!rc) rc = run_body(v, 0, 1, v->prefetch);
+  if (!rc && hipStreamSynchronize(v->st) != hipSuccess) rc = RL_E_DEVICE;
+  v->suffix.assign(L, nullptr);
+  v->single.assign(L, nullptr);
+  v->single_pf.assign(v->prefetch ? L - 1 : 0, nullptr);
+  for (int l = 0; l < L && !rc; ++l) {
+    rc = capture(v, l, L, false, &v->suffix[l]);
+    if (!rc) rc = capture(v, l, l + 1, false, &v->single[l]);
+    if (!rc && v->prefetch && l + 1 < L) rc = capture(v, l, l + 1, true, &v->single_pf[l]);
+  }
+  if (rc) {
+    release(v);
+    return nullptr;
+  }
+  return v;
+}
+
+int rl_driver_token(rl_decode_driver* v, const float* x0) {
+  if (!v || !x0) return RL_E_INVAL;
+  if (v->broken) return RL_E_STATE;
+  const int rc = token(v, x0);
+  if (rc) v->broken = true;   // an interrupted token leaves cache and pool out of step
+  return rc;
+}
+
+int rl_driver_stats(const rl_decode_driver* v, int64_t* out) {
+  if (!v || !out) return RL_E_INVAL;
+  for (int i = 0; i < 8; ++i) out[i] = v->stats[i];
+  return RL_OK;
+}
+
+void rl_driver_destroy(rl_decode_driver* v) {
+  if (!v) return;
+  (void)hipStreamSynchronize(v->st);
+  release(v);
+}
+
+}  // extern "C"

@@ -103,5 +103,6 @@ void launch_residual_rmsnorm(int T, int H, const float* x, const float* y,
 void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t* early_out,
                          hipStream_t st);
 void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st);
+void launch_table_scatter(int32_t* table, const int32_t* pairs, int n, hipStream_t st);
 
 }  // namespace rl

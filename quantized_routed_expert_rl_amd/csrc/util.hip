@@ -106,6 +106,18 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// table[pairs[2i]] = pairs[2i+1] for i < n (residency entries that a load
+// or an eviction changed; keys are distinct).
+__global__ __launch_bounds__(64) void table_scatter_kernel(int32_t* __restrict__ table,
+                                                           const int32_t* __restrict__ pairs,
+                                                           int n) {
+  for (int i = threadIdx.x; i < n; i += 64) table[pairs[2 * i]] = pairs[2 * i + 1];
+}
+
+void launch_table_scatter(int32_t* table, const int32_t* pairs, int n, hipStream_t st) {
+  table_scatter_kernel<<<1, 64, 0, st>>>(table, pairs, n);
+}
+
 void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st) {
   stream_read_kernel<<<8 * n_cu, 256, 0, st>>>(static_cast<const uint4*>(buf), bytes / 16, sink);
 }

@@ -351,3 +351,40 @@ class ServicedDecodeStack:
         elif n_eo == 0:
             self.sync_path = False
         return s.x[self.L]
+
+
+class NativeServicedDecode:
+    """The miss-servicing decode of ``ServicedDecodeStack`` run by the
+    library's native driver (rl_driver_*): the same policy, graphs and
+    statistics, with the per-layer host work (waits, cache calls, copies,
+    table updates) in C++ instead of Python.  ``x`` [L+1, H] holds every
+    layer's input after a token."""
+
+    def __init__(self, model: DeviceModel, store: "HostExpertStore", early_out_limit: int = 4,
+                 prefetch: bool = False, sticky: bool = False):
+        w = model.w
+        self.model, self.store = model, store
+        self.L, self.H = w.n_layers, w.hidden
+        d = model.desc
+        self.desc = B.desc(d.hidden, d.n_experts, d.top_k, d.width, d.n_layers, d.qbits, d.n_slots,
+                           flags=B.RL_STICKY_EARLY_OUT if sticky else 0)
+        self.cache = B.ExpertCache(int(model.pool.shape[0]), self.L, w.n_experts)
+        for l, e in zip(*np.nonzero(model.table >= 0)):
+            self.cache.insert(int(l), int(e), int(model.table[l, e]))
+        self.x = torch.empty(self.L + 1, self.H, device=DEV)
+        self.stream = torch.cuda.Stream()
+        self.drv = B.DecodeDriver(self.desc, [model.router[l] for l in range(self.L)],
+                                  [model.bias[l] for l in range(self.L)], model.residency,
+                                  model.pool, store.tensor, self.cache, self.x,
+                                  early_out_limit=early_out_limit, prefetch=prefetch, eps=EPS,
+                                  stream=self.stream)
+
+    def token(self, x0: torch.Tensor) -> torch.Tensor:
+        x0 = x0.reshape(self.H)
+        self.stream.wait_stream(torch.cuda.current_stream())
+        self.drv.token(x0)
+        return self.x[self.L]
+
+    @property
+    def stats(self) -> dict:
+        return self.drv.stats()

@@ -1,0 +1,58 @@
+"""The native decode driver (rl_driver_*) against the Python miss-servicing
+stack ("Red Lite dev23 - per-layer early-out and pre-gated expert prefetch",
+"What changed": stop at the first missing layer, load its experts, run it
+again, resume; the early-out / layer-by-layer policy; the pre-gated
+prefetch).  Both drive the same kernels with the same policy from the same
+seeded model, so every layer's input after every token, the statistics, the
+cache's counters and the device residency table must agree exactly; the
+layer inputs must also equal those of an all-resident stack."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_routed_expert_rl_amd import synth
+from quantized_routed_expert_rl_amd.device import DeviceModel, to_dev
+from quantized_routed_expert_rl_amd.stack import (DecodeStack, HostExpertStore,
+                                                  NativeServicedDecode, ServicedDecodeStack)
+from quantized_routed_expert_rl_amd.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _workloads(per_layer):
+    hot = Workload("serviced", 9, 256, 32, 4, 256, 6, 10, zipf=True, resident=6 * per_layer,
+                   popular=True)
+    full = Workload(**{**hot.__dict__, "resident": -1, "popular": False})
+    return hot, full
+
+
+@pytest.mark.parametrize("per_layer,limit,prefetch,sticky", [
+    (8, 4, False, False), (8, 0, False, False), (16, 4, False, False), (8, 0, True, False),
+    (8, 4, False, True), (8, 0, True, True), (8, 100, False, True)])
+def test_native_driver_equals_python_stack(per_layer, limit, prefetch, sticky):
+    hot, full = _workloads(per_layer)
+    xs = synth.activations(hot, hot.tokens)
+    ref = DecodeStack(DeviceModel(full))
+    store = HostExpertStore(hot)
+    py = ServicedDecodeStack(DeviceModel(hot), store, early_out_limit=limit, prefetch=prefetch,
+                             sticky=sticky)
+    nat = NativeServicedDecode(DeviceModel(hot), store, early_out_limit=limit, prefetch=prefetch,
+                               sticky=sticky)
+    for t in range(hot.tokens):
+        print("token", t, flush=True)
+        x0 = to_dev(xs[t])
+        ref.token(x0)
+        py.token(x0)
+        nat.token(x0)
+        torch.cuda.synchronize()
+        want = ref.x.cpu().numpy()
+        assert np.array_equal(py.stack.x.cpu().numpy(), want), f"python stack, token {t}"
+        assert np.array_equal(nat.x.cpu().numpy(), want), f"native driver, token {t}"
+    assert nat.stats == py.stats, (nat.stats, py.stats)
+    assert nat.cache.stats() == py.cache.stats()
+    assert np.array_equal(nat.model.residency.cpu().numpy(), nat.cache.table())
+    assert np.array_equal(nat.cache.table(), py.cache.table())
+    st = nat.stats
+    assert st["loads"] > 0 and st["early_outs"] > 0
+    if prefetch:
+        assert st["predictions"] > 0 and st["prefetch_loads"] > 0

@@ -105,3 +105,16 @@ def test_errors_before_any_launch():
     assert B.lib.rl_stream_read(None, 1 << 20, 0x1000, None) == B.RL_E_INVAL
     assert B.lib.rl_stream_read(0x1000, 1000, 0x1000, None) == B.RL_E_RANGE   # not a multiple of 16
     assert B.lib.rl_strerror(B.RL_E_SCRATCH).decode() == "scratch buffer too small"
+
+
+def test_driver_argument_checks():
+    """The decode driver's entry points reject missing arguments before any
+    device work (no GPU needed)."""
+    import ctypes as C
+    assert B.lib.rl_driver_create(None, None) is None
+    assert B.lib.rl_driver_token(None, None) == -1
+    out = (C.c_int64 * 8)()
+    assert B.lib.rl_driver_stats(None, out) == -1
+    B.lib.rl_driver_destroy(None)
+    cfg = B.RlDriverConfig()                 # every pointer NULL
+    assert B.lib.rl_driver_create(C.byref(cfg), None) is None
