@@ -81,8 +81,6 @@ struct rl_decode_driver {
 
 namespace {
 
-int nflags(const rl_decode_driver* v) { return v->sticky ? 1 : v->L; }
-
 rl_route_out layer_route(const rl_decode_driver* v, int l) {
   rl_route_out o;
   o.ids = v->ids + l * v->k;
@@ -118,23 +116,19 @@ int run_predict(rl_decode_driver* v, int l) {
                   v->residency, &o, v->pscratch, v->pscratch_bytes, v->st);
 }
 
-int run_mirror(rl_decode_driver* v, bool predict) {
-  hipError_t e = hipMemcpyAsync(v->h_flags, v->flags, sizeof(uint32_t) * nflags(v),
-                                hipMemcpyDeviceToHost, v->st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(v->h_miss, v->miss, sizeof(uint32_t) * v->L, hipMemcpyDeviceToHost, v->st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(v->h_ids, v->ids, sizeof(int32_t) * v->L * v->k, hipMemcpyDeviceToHost,
-                       v->st);
-  if (e == hipSuccess && predict)
-    e = hipMemcpyAsync(v->h_pids, v->pids, sizeof(int32_t) * v->k, hipMemcpyDeviceToHost, v->st);
-  return e == hipSuccess ? RL_OK : RL_E_DEVICE;
+// flags [L], miss counts [L], ids [L x k] and predicted ids [k] sit back to
+// back on the device and in the pinned mirror: one copy moves them all
+int run_mirror(rl_decode_driver* v) {
+  const size_t n = sizeof(int32_t) * (2 * v->L + (v->L + 1) * v->k);
+  return hipMemcpyAsync(v->h_flags, v->flags, n, hipMemcpyDeviceToHost, v->st) == hipSuccess
+             ? RL_OK
+             : RL_E_DEVICE;
 }
 
 int run_body(rl_decode_driver* v, int l0, int l1, bool predict) {
   int rc = predict ? run_predict(v, l0) : RL_OK;
   for (int l = l0; l < l1 && !rc; ++l) rc = run_layer(v, l);
-  return rc ? rc : run_mirror(v, predict);
+  return rc ? rc : run_mirror(v);
 }
 
 int capture(rl_decode_driver* v, int l0, int l1, bool predict, hipGraphExec_t* out) {
@@ -362,15 +356,16 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   v->pscratch_bytes = rl_route_scratch_bytes(&v->dr, 1);
   // one device allocation, every part 256-byte aligned
   auto up = [](int64_t n) { return (n + 255) & ~int64_t(255); };
-  const int64_t o_a = 0, o_y = o_a + up(4 * (L + 1) * H), o_ids = o_y + up(4 * L * H),
-                o_slots = o_ids + up(4 * L * k), o_wts = o_slots + up(4 * L * k),
-                o_miss = o_wts + up(4 * L * k), o_flags = o_miss + up(4 * L),
-                o_pids = o_flags + up(4 * L), o_pslots = o_pids + up(4 * k),
+  // flags, miss, ids, pids contiguous (one mirror copy)
+  const int64_t o_a = 0, o_y = o_a + up(4 * (L + 1) * H), o_flags = o_y + up(4 * L * H),
+                o_miss = o_flags + 4 * L, o_ids = o_miss + 4 * L, o_pids = o_ids + 4 * L * k,
+                o_slots = o_flags + up(4 * (2 * L + (L + 1) * k)),
+                o_wts = o_slots + up(4 * L * k), o_pslots = o_wts + up(4 * L * k),
                 o_pw = o_pslots + up(4 * k), o_pmiss = o_pw + up(4 * k), o_pflag = o_pmiss + 256,
                 o_pairs = o_pflag + 256, o_scr = o_pairs + up(4 * 4 * k),
                 o_pscr = o_scr + up(v->scratch_bytes), dev_bytes = o_pscr + up(v->pscratch_bytes);
-  const int64_t h_flags = 0, h_miss = h_flags + up(4 * L), h_ids = h_miss + up(4 * L),
-                h_pids = h_ids + up(4 * L * k), h_pairs = h_pids + up(4 * k),
+  const int64_t h_flags = 0, h_miss = h_flags + 4 * L, h_ids = h_miss + 4 * L,
+                h_pids = h_ids + 4 * L * k, h_pairs = up(h_pids + 4 * k),
                 h_table = h_pairs + up(4 * 4 * k), host_bytes = h_table + up(4 * int64_t(L) * v->E);
   if (hipMalloc(&v->dev, dev_bytes) != hipSuccess) v->dev = nullptr;
   if (hipHostMalloc(&v->host, host_bytes, hipHostMallocDefault) != hipSuccess) v->host = nullptr;
