@@ -144,7 +144,8 @@ def test_decode_reruns_bit_identical(real):
 
 @pytest.mark.parametrize("H,E,k,F,qbits", [
     (256, 16, 2, 64, 3), (512, 100, 5, 128, 2), (1024, 1024, 32, 256, 2),
-    (256, 8, 1, 32, 3), (2048, 64, 8, 2048, 2), (512, 200, 7, 1024, 3)])
+    (256, 8, 1, 32, 3), (2048, 64, 8, 2048, 2), (512, 200, 7, 1024, 3),
+    (256, 1, 1, 64, 2), (512, 6, 6, 256, 3)])       # one expert; every expert selected
 def test_decode_shapes(H, E, k, F, qbits):
     rng = np.random.default_rng(H + E + k + F + qbits)
     n = H * F

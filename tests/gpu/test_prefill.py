@@ -145,7 +145,8 @@ def test_prefill_early_out(real):
 
 @pytest.mark.parametrize("H,E,k,F,qbits,T,cap", [
     (256, 16, 2, 64, 3, 9, 16), (512, 100, 5, 128, 2, 33, 20), (1024, 1024, 32, 256, 2, 17, 1024),
-    (256, 8, 1, 32, 3, 70, 3), (2048, 64, 8, 2048, 2, 12, 64), (512, 200, 7, 1024, 3, 21, 30)])
+    (256, 8, 1, 32, 3, 70, 3), (2048, 64, 8, 2048, 2, 12, 64), (512, 200, 7, 1024, 3, 21, 30),
+    (256, 1, 1, 64, 2, 19, 1), (512, 6, 6, 256, 3, 40, 6)])   # one expert; every expert selected
 def test_prefill_shapes(H, E, k, F, qbits, T, cap):
     rng = np.random.default_rng(H + E + k + F + qbits + T)
     n = H * F
