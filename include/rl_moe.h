@@ -175,6 +175,26 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x,
                      const rl_route_out* route, void* scratch,
                      int64_t scratch_bytes, float* y, void* stream);
 
+/* moe_decode_layer with in-place reads of missing experts: a selected expert
+ * that is not resident is read where it lies in `host_store` (pinned, mapped
+ * host memory holding every expert of every layer: row layer * E + expert,
+ * rl_slot_bytes each, 256-byte aligned), by the same kernels over PCIe,
+ * instead of stopping the layer.  The notes load misses into GPU-visible
+ * buffers before running them, and tried reading experts in place from a
+ * mapping as an option ("Red Lite dev20 - batched prompt ingestion", expert
+ * kernel layout: numerically identical, slower on their machine); here the
+ * pinned store is read directly, so a token needs no host round trip.
+ * miss_count still counts the selections served from host memory; the flag
+ * stays 0 and y is always written.  Matrix-core shapes only (width a
+ * multiple of 256: else RL_E_SHAPE); RL_E_INVAL for a NULL or misaligned
+ * host_store, one the device cannot map (hipHostGetDevicePointer fails), or
+ * RL_STICKY_EARLY_OUT in the descriptor. */
+int moe_decode_layer_mapped(const rl_moe_desc* d, int32_t layer, const float* x,
+                            const float* router_w, const float* router_bias,
+                            const int32_t* residency, const void* slot_pool,
+                            const void* host_store, const rl_route_out* route, void* scratch,
+                            int64_t scratch_bytes, float* y, void* stream);
+
 /* One prefill chunk of n_tokens tokens through layer `layer` (dev20 "What
  * changed"): route every token, build the chunk's plan -- consecutive token
  * groups whose union of selected experts stays within plan_cap (a token

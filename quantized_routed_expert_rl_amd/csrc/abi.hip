@@ -298,6 +298,37 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x, const 
   return launch_status();
 }
 
+int moe_decode_layer_mapped(const rl_moe_desc* d, int32_t layer, const float* x,
+                            const float* router_w, const float* router_bias,
+                            const int32_t* residency, const void* slot_pool,
+                            const void* host_store, const rl_route_out* route, void* scratch,
+                            int64_t scratch_bytes, float* y, void* stream) {
+  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
+  if (rc) return rc;
+  if (!slot_pool || !y || !host_store || !aligned(slot_pool, 256) || !aligned(y, 16) ||
+      !aligned(host_store, 256) || (d->flags & RL_STICKY_EARLY_OUT))
+    return RL_E_INVAL;
+  if (d->width % 256) return RL_E_SHAPE;            // matrix-core shapes only
+  // the device-visible address of the host store (pinned, mapped memory only)
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0) != hipSuccess || !dev) {
+    (void)hipGetLastError();   // the failed lookup must not surface at the caller's next call
+    return RL_E_INVAL;
+  }
+  const DecodeLayout l = decode_layout(d, 1);
+  if (scratch_bytes < l.total) return RL_E_SCRATCH;
+  uint8_t* s = static_cast<uint8_t*>(scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeArgs da = decode_args(d, layer, x, router_w, router_bias, residency, slot_pool, route, s,
+                              l, y);
+  if (!da.mfma) return RL_E_SHAPE;
+  da.host = static_cast<const uint8_t*>(dev) + int64_t(layer) * d->n_experts * da.pool.slot_bytes;
+  launch_decode_router(da, st);
+  launch_decode_gateup(da, st);
+  launch_decode_down_sum(da, st);
+  return launch_status();
+}
+
 int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int32_t plan_cap,
                       const float* x, const float* router_w, const float* router_bias,
                       const int32_t* residency, const void* slot_pool, const rl_route_out* route,

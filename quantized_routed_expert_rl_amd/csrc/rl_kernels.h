@@ -42,6 +42,10 @@ struct DecodeArgs {
   float* y;
   bool mfma;            // int8 matrix-core expert kernels (F % 256 == 0)
   bool sticky;          // early_out shared and only raised: a set flag stops the call
+  // in-place reads: non-resident experts of this layer are read from host
+  // memory at host + expert * slot_bytes (device-visible address), and the
+  // flag stays clear; NULL = early-out on a miss
+  const uint8_t* host = nullptr;
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);

@@ -91,7 +91,13 @@ class DeviceModel:
         return B.rl_route(self.desc, layer, x.shape[0], x, self.router[layer], self.bias[layer],
                           self.residency, out.c(), scratch, scratch.numel(), stream)
 
-    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None, desc=None):
+    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None, desc=None,
+               host_store=None):
+        if host_store is not None:            # missing experts read in place
+            return B.moe_decode_layer_mapped(desc or self.desc, layer, x, self.router[layer],
+                                             self.bias[layer], self.residency, self.pool,
+                                             host_store, out.c(), scratch, scratch.numel(), y,
+                                             stream)
         return B.moe_decode_layer(desc or self.desc, layer, x, self.router[layer], self.bias[layer],
                                   self.residency, self.pool, out.c(), scratch, scratch.numel(),
                                   y, stream)

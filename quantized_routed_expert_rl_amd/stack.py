@@ -34,9 +34,12 @@ class DecodeStack:
     its normalised input, ``routes[l]`` its routing results and ``y[l]`` its
     MoE output (left untouched when the layer's flag is set)."""
 
-    def __init__(self, model: DeviceModel):
+    def __init__(self, model: DeviceModel, host_store=None):
         w = model.w
         self.model = model
+        # a pinned store of every expert: missing experts are read from it in
+        # place (moe_decode_layer_mapped) and no layer stops
+        self.host_store = host_store
         self.L, self.H = w.n_layers, w.hidden
         self.x = torch.empty(self.L + 1, self.H, device=DEV)
         self.a = torch.empty(self.L + 1, self.H, device=DEV)   # a[L]: norm of the output
@@ -50,7 +53,8 @@ class DecodeStack:
         self.x[0].copy_(x0.reshape(self.H))
         B.rl_rmsnorm(1, self.H, self.x[0], self.a[0], EPS)
         for l in range(self.L):
-            self.model.decode(l, self.a[l], self.routes[l], self.scratch, self.y[l])
+            self.model.decode(l, self.a[l], self.routes[l], self.scratch, self.y[l],
+                              host_store=self.host_store)
             B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
                                   self.x[l + 1], self.a[l + 1], EPS)
         return self.x[self.L]

@@ -1,0 +1,104 @@
+"""In-place reads of missing experts (moe_decode_layer_mapped): a selected
+expert that is not resident is read from the pinned host store by the same
+kernels, so the layer's output equals that of a fully resident layer bit for
+bit, the miss count still counts those selections, and the flag stays clear
+("Red Lite dev20 - batched prompt ingestion", expert kernel layout: reading
+experts in place is numerically identical)."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_routed_expert_rl_amd import binding as B
+from quantized_routed_expert_rl_amd import synth
+from quantized_routed_expert_rl_amd.device import DeviceModel, RouteBuffers, to_dev
+from quantized_routed_expert_rl_amd.stack import DecodeStack, HostExpertStore
+from quantized_routed_expert_rl_amd.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _workloads(per_layer, qbits=2):
+    hot = Workload("serviced", 9, 256, 32, 4, 256, 6, 10, zipf=True, resident=6 * per_layer,
+                   popular=True, qbits=qbits)
+    full = Workload(**{**hot.__dict__, "resident": -1, "popular": False})
+    return hot, full
+
+
+@pytest.mark.parametrize("qbits", [2, 3])
+def test_mapped_layer_equals_resident_layer(qbits):
+    hot, full = _workloads(4, qbits)
+    store = HostExpertStore(hot)
+    mh, mf = DeviceModel(hot), DeviceModel(full)
+    xs = synth.activations(hot, hot.tokens)
+    sh, sf = mh.decode_scratch(), mf.decode_scratch()
+    total_miss = 0
+    for t in range(hot.tokens):
+        for l in range(hot.n_layers):
+            x = to_dev(xs[t])
+            oh = RouteBuffers.alloc(1, hot.top_k, hot.n_experts)
+            of = RouteBuffers.alloc(1, hot.top_k, hot.n_experts)
+            yh = torch.full((hot.hidden,), float("nan"), device="cuda")
+            yf = torch.full((hot.hidden,), float("nan"), device="cuda")
+            mh.decode(l, x, oh, sh, yh, host_store=store.tensor)
+            mf.decode(l, x, of, sf, yf)
+            torch.cuda.synchronize()
+            assert torch.equal(oh.ids, of.ids)
+            assert torch.equal(yh, yf), f"token {t} layer {l}"
+            ids = oh.ids.cpu().numpy()[0]
+            want_miss = int((mh.table[l][ids] < 0).sum())
+            assert int(oh.miss_count.cpu()[0]) == want_miss
+            assert int(oh.early_out.cpu()[0]) == 0
+            slots = oh.slots.cpu().numpy()[0]
+            assert np.array_equal(slots < 0, mh.table[l][ids] < 0)
+            total_miss += want_miss
+    assert total_miss > 0
+
+
+def test_mapped_stack_equals_resident_stack():
+    hot, full = _workloads(8)
+    store = HostExpertStore(hot)
+    ref = DecodeStack(DeviceModel(full))
+    st = DecodeStack(DeviceModel(hot), host_store=store.tensor)
+    xs = synth.activations(hot, hot.tokens)
+    misses = 0
+    for t in range(hot.tokens):
+        ref.token(to_dev(xs[t]))
+        st.token(to_dev(xs[t]))
+        torch.cuda.synchronize()
+        assert torch.equal(st.x, ref.x), f"token {t}"
+        misses += sum(int(r.miss_count.cpu()[0]) for r in st.routes)
+        assert all(int(r.early_out.cpu()[0]) == 0 for r in st.routes)
+    assert misses > 0
+
+
+def test_mapped_argument_checks():
+    hot, _ = _workloads(4)
+    m = DeviceModel(hot)
+    store = HostExpertStore(hot)
+    out = RouteBuffers.alloc(1, hot.top_k, hot.n_experts)
+    y = torch.empty(hot.hidden, device="cuda")
+    sc = m.decode_scratch()
+    x = to_dev(synth.activations(hot, 1)[0])
+    d = m.desc
+
+    def call(desc, host):
+        return B.lib.moe_decode_layer_mapped(C.byref(desc), 0, x.data_ptr(), m.router[0].data_ptr(),
+                                             None, m.residency.data_ptr(), m.pool.data_ptr(), host,
+                                             C.byref(out.c()), sc.data_ptr(), sc.numel(),
+                                             y.data_ptr(), None)
+    assert call(d, None) == -1                                     # no host store
+    pageable = np.zeros(1 << 20, np.uint8)
+    addr = (pageable.ctypes.data + 255) & ~255
+    assert call(d, addr) == -1                                     # not pinned and mapped
+    sticky = B.desc(d.hidden, d.n_experts, d.top_k, d.width, d.n_layers, d.qbits, d.n_slots,
+                    flags=B.RL_STICKY_EARLY_OUT)
+    assert call(sticky, store.tensor.data_ptr()) == -1
+    valu = B.desc(d.hidden, d.n_experts, d.top_k, 64, d.n_layers, d.qbits, d.n_slots)
+    sc2 = torch.zeros(B.rl_decode_scratch_bytes(valu), dtype=torch.uint8, device="cuda")
+    rc = B.lib.moe_decode_layer_mapped(C.byref(valu), 0, x.data_ptr(), m.router[0].data_ptr(), None,
+                                       m.residency.data_ptr(), m.pool.data_ptr(),
+                                       store.tensor.data_ptr(), C.byref(out.c()), sc2.data_ptr(),
+                                       sc2.numel(), y.data_ptr(), None)
+    assert rc == -2                                                # width 64: no matrix-core path
