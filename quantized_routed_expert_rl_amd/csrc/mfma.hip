@@ -6,6 +6,8 @@
 //
 // The int8 operands and their exactness are described in rl_mfma.h; columns
 // of the B operand are 4 * token + digit.
+#include <type_traits>
+
 #include "rl_common.h"
 #include "rl_kernels.h"
 #include "rl_mfma.h"
@@ -250,6 +252,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
 
   int staged = -1;                       // item whose operands are in LDS
   int item = 0, tile = 0;                // the current round's item and this wave's tile
+  bool two = true;                       // the pass has more than 8 tokens (both MFMA groups)
   float acc[kCT][4];
   for (int q0 = 0; q0 < NQ; q0 += NS)
 #pragma unroll
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
         const int p0 = bucket_start[b], n = bucket_start[b + 1] - p0;
         const int c0 = (item - item_start[b]) * kPassTok;
         const int nt = n - c0 < kPassTok ? n - c0 : kPassTok;
+        two = nt > 8;
         if (tid < kPassTok) {
           const int pos = p0 + c0 + tid;
           const int src = tid < nt ? (GATEUP ? pairs[pos] / k : pos) : -1;
@@ -301,12 +305,18 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[ct][m] = 0.f;
     }
+    // one step for kc groups of 8 tokens: with 3-bit codes, passes of at most
+    // 8 tokens skip the second group's MFMAs, scaling and digit reads (with
+    // 2-bit codes the second copy of the step costs more than it saves:
+    // measured, 5 % slower)
+    auto step = [&](auto kc_tag) __attribute__((always_inline)) {
+    constexpr int kc = decltype(kc_tag)::value;
     const RowLuts<QBITS> luts = row_luts<QBITS>(ca, ssel);
     // the lane's row's block factor: half (block parity) of the d dword
     const float rs = dh_dq<QBITS>((KB == 1 ? rowoff & 1 : kb & 1) ? ca.dh >> 16 : ca.dh & 0xffffu);
-    v16i D[kCT];
+    v16i D[kc];
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) D[ct] = v16i{};
+    for (int ct = 0; ct < kc; ++ct) D[ct] = v16i{};
     // digit operands read one MFMA step ahead, so no MFMA waits on its own
     // LDS read.  Chunk of token c/4, digit c%4, run 8h + nn: 512h + 64(c%4) +
     // 256(nn/4) + 16(nn%4) bytes into the token's K-block.
@@ -316,20 +326,20 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
                                                     256 * (nn >> 2) + 16 * (nn & 3));
       return v4i{v.x, v.y, v.z, v.w};
     };
-    v4i Ad[2][kCT];
+    v4i Ad[2][kc];
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) Ad[0][ct] = aread(0, ct);
+    for (int ct = 0; ct < kc; ++ct) Ad[0][ct] = aread(0, ct);
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       if (nn < 7) {
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) Ad[(nn + 1) & 1][ct] = aread(nn + 1, ct);
+        for (int ct = 0; ct < kc; ++ct) Ad[(nn + 1) & 1][ct] = aread(nn + 1, ct);
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's MFMAs
       v4i W, G;
       row_operand<QBITS>(ca, luts, nn, W, G);
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) {
+      for (int ct = 0; ct < kc; ++ct) {
         D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ad[nn & 1][ct], W, D[ct], 0, 0, 0);
         if (QBITS == 3)
           D[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ad[nn & 1][ct], G, D[ct], 0, 0, 0);
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
     // pairs 256 D0 + D1 and 256 D2 + D3 stay below 2^31, so each token takes
     // two conversions and one scaled add per block
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct)
+    for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int hi = D[ct][4 * m] * 256 + D[ct][4 * m + 1];
@@ -348,9 +358,9 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
       }
     if (kb == KB - 1) {
       // tile done: the lane holds row c of the tile for tokens 8ct + 2m + h
-      float v[kCT][4];
+      float v[kc][4];
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct)
+      for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
         for (int m = 0; m < 4; ++m) v[ct][m] = acc[ct][m] * s_cs[8 * ct + 2 * m + h];
       if (GATEUP) {
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
         const bool gl = c < 16;
         const int j = 16 * tile + (c & 15);
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct)
+        for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const float other = __shfl_xor(gl ? v[ct][2 + i] : v[ct][i], 16);
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
       } else {
         const int i0 = 32 * tile + c;
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct)
+        for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const int dst = s_dst[8 * ct + 2 * m + h];
@@ -378,6 +388,11 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
           }
       }
     }
+    };
+    if (QBITS == 2 || two)
+      step(std::integral_constant<int, 2>{});
+    else
+      step(std::integral_constant<int, 1>{});
   }
 }
 
