@@ -241,6 +241,45 @@ def main():
         g.replay()
         return g
 
+    # ------------------------------------------- decode, 3-bit block weights
+    # the same single-token decode with the heavier 3-bit format (eight code
+    # levels): 1.45x the expert bytes per token
+    del g2, scr, outs2, rb2
+    w3b = workloads.get("decode_1l", 3)
+    m3b = DeviceModel(w3b)
+    T3b = min(T, 128)
+    X3b = to_dev(synth.activations(w3b, T3b, stream=1))
+    Y3b = torch.empty(T3b, w3b.hidden, device="cuda")
+    rb3 = RouteBuffers.alloc(T3b, w3b.top_k, w3b.n_experts, with_logits=False)
+    outs3 = [B.route_out(rb3.ids[t], rb3.weights[t], rb3.slots[t], rb3.miss_count, rb3.early_out)
+             for t in range(T3b)]
+    sc3 = m3b.decode_scratch()
+    d3b = m3b.desc
+
+    def decode3():
+        st = torch.cuda.current_stream().cuda_stream
+        for t in range(T3b):
+            rc = lib.moe_decode_layer(C.byref(d3b), 0, X3b[t].data_ptr(), m3b.router[0].data_ptr(),
+                                      None, m3b.residency.data_ptr(), m3b.pool.data_ptr(),
+                                      C.byref(outs3[t]), sc3.data_ptr(), sc3.numel(),
+                                      Y3b[t].data_ptr(), st)
+            if rc:
+                raise B.RlError(f"moe_decode_layer {rc}")
+
+    with torch.cuda.stream(stream):
+        decode3()
+        stream.synchronize()
+        g3 = graph_of(decode3)
+        ms3 = event_ms(g3.replay, stream, 5)
+    assert int(rb3.early_out.cpu()[0]) == 0 and torch.isfinite(Y3b).all()
+    line["decode_3bit"] = {
+        "tokens_per_s": round(T3b / (ms3 * 1e-3), 1), "us_per_token": round(ms3 * 1e3 / T3b, 3),
+        "layer_bytes_per_token": w3b.top_k * 3 * B.rl_tensor_bytes(d3b) + w3b.n_experts * w3b.hidden * 4
+                                 + 2 * w3b.hidden * 4,
+        "workload": f"decode_1l with 3-bit block weights: {T3b} independent tokens per graph replay"}
+    del g3, m3b, X3b, Y3b, rb3, outs3, sc3
+    torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ prefill
     if not args.no_prefill:
         w3 = workloads.get("prefill_1l")
