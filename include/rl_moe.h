@@ -212,6 +212,22 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
                       void* scratch, int64_t scratch_bytes, float* y,
                       void* stream);
 
+/* moe_prefill_chunk with in-place reads of missing experts: a bucket whose
+ * expert is not resident is read by the expert kernels where it lies in
+ * `host_store` (pinned, mapped host memory holding every expert of every
+ * layer: row layer * E + expert, rl_slot_bytes each, 256-byte aligned),
+ * once per pass of its tokens, instead of stopping the chunk (the notes'
+ * optional in-place reading, "Red Lite dev20 - batched prompt ingestion",
+ * expert kernel layout).  miss_count still counts the selections served
+ * from host memory; the flag stays 0 and y is always written.  Same shapes
+ * and errors as moe_decode_layer_mapped (matrix-core shapes only). */
+int moe_prefill_chunk_mapped(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
+                             int32_t plan_cap, const float* x, const float* router_w,
+                             const float* router_bias, const int32_t* residency,
+                             const void* slot_pool, const void* host_store,
+                             const rl_route_out* route, void* scratch, int64_t scratch_bytes,
+                             float* y, void* stream);
+
 /* Stage entry points, for tests and benchmarks: each enqueues the kernels of
  * one step of a path above, with the same arguments and scratch layout.
  *   rl_decode_stage: stage 0 = router GEMV into scratch; stage 1 = softmax

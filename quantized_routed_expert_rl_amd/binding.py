@@ -65,6 +65,10 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
                                     C.c_void_p]),
+    "moe_prefill_chunk_mapped": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.POINTER(RlRouteOut),
+                                           C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "rl_decode_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
@@ -204,6 +208,16 @@ def moe_decode_layer_mapped(d, layer, x, router_w, router_bias, residency, slot_
                                              _ptr(host_store), C.byref(route), _ptr(scratch),
                                              scratch_bytes, _ptr(y), _stream(stream)),
                  "moe_decode_layer_mapped")
+
+
+def moe_prefill_chunk_mapped(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,
+                             slot_pool, host_store, route: RlRouteOut, scratch, scratch_bytes, y,
+                             stream=None) -> int:
+    return check(lib.moe_prefill_chunk_mapped(C.byref(d), layer, n_tokens, plan_cap, _ptr(x),
+                                              _ptr(router_w), _ptr(router_bias), _ptr(residency),
+                                              _ptr(slot_pool), _ptr(host_store), C.byref(route),
+                                              _ptr(scratch), scratch_bytes, _ptr(y),
+                                              _stream(stream)), "moe_prefill_chunk_mapped")
 
 
 def moe_prefill_chunk(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,

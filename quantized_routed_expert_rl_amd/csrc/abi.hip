@@ -203,6 +203,7 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
   a.mfma = d->width % 256 == 0;
   a.tile_tokens = a.mfma ? 16 : 8;   // tokens per matrix-core pass / VALU tile
   a.y = y;
+  a.n_slots = d->n_slots;
   return a;
 }
 
@@ -347,6 +348,43 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int
   launch_route(ra, st);
   const PrefillArgs a = prefill_args(d, layer, n_tokens, plan_cap, x, residency, slot_pool, route,
                                      s, l, y);
+  launch_prefill_plan(a, st);
+  launch_prefill_gateup(a, st);
+  launch_prefill_down(a, st);
+  launch_prefill_sum(a, st);
+  return launch_status();
+}
+
+int moe_prefill_chunk_mapped(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
+                             int32_t plan_cap, const float* x, const float* router_w,
+                             const float* router_bias, const int32_t* residency,
+                             const void* slot_pool, const void* host_store,
+                             const rl_route_out* route, void* scratch, int64_t scratch_bytes,
+                             float* y, void* stream) {
+  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
+  if (rc) return rc;
+  if (!slot_pool || !y || !host_store || !aligned(slot_pool, 256) || !aligned(y, 16) ||
+      !aligned(host_store, 256) || (d->flags & RL_STICKY_EARLY_OUT))
+    return RL_E_INVAL;
+  if (d->width % 256) return RL_E_SHAPE;            // matrix-core shapes only
+  if (n_tokens < 1 || plan_cap < d->top_k) return RL_E_RANGE;
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0) != hipSuccess || !dev) {
+    (void)hipGetLastError();   // the failed lookup must not surface at the caller's next call
+    return RL_E_INVAL;
+  }
+  const PrefillLayout l = prefill_layout(d, n_tokens);
+  if (scratch_bytes < l.total) return RL_E_SCRATCH;
+  uint8_t* s = static_cast<uint8_t*>(scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  RouteArgs ra = route_args(d, layer, n_tokens, x, router_w, router_bias, residency, route,
+                            reinterpret_cast<float*>(s + l.logits));
+  ra.flag_misses = false;                           // misses are read in place
+  launch_route(ra, st);
+  PrefillArgs a = prefill_args(d, layer, n_tokens, plan_cap, x, residency, slot_pool, route, s, l,
+                               y);
+  if (!a.mfma) return RL_E_SHAPE;
+  a.host = static_cast<const uint8_t*>(dev) + int64_t(layer) * d->n_experts * a.pool.slot_bytes;
   launch_prefill_plan(a, st);
   launch_prefill_gateup(a, st);
   launch_prefill_down(a, st);

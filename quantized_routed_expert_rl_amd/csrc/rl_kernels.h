@@ -21,6 +21,7 @@ struct RouteArgs {
   int32_t* slots;
   uint32_t* miss_count;
   uint32_t* early_out;
+  bool flag_misses = true;   // false: misses are counted but raise no flag (in-place reads)
 };
 void launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -90,6 +91,10 @@ struct PrefillArgs {
   uint8_t* hq;      // [T*k][F*4] digit operands of h (MFMA path)
   int32_t* he;      // [T*k][F/256] exponents of h
   float* y;
+  int n_slots = 0;
+  // in-place reads: non-resident experts of this layer are read from host
+  // memory at host + expert * slot_bytes (device-visible address); NULL = none
+  const uint8_t* host = nullptr;
 };
 void launch_prefill_plan(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_gateup(const PrefillArgs& a, hipStream_t st);

@@ -102,7 +102,13 @@ class DeviceModel:
                                   self.residency, self.pool, out.c(), scratch, scratch.numel(),
                                   y, stream)
 
-    def prefill(self, layer, x, plan_cap, out: RouteBuffers, scratch, y, stream=None):
+    def prefill(self, layer, x, plan_cap, out: RouteBuffers, scratch, y, stream=None,
+                host_store=None):
+        if host_store is not None:            # missing experts read in place
+            return B.moe_prefill_chunk_mapped(self.desc, layer, x.shape[0], plan_cap, x,
+                                              self.router[layer], self.bias[layer],
+                                              self.residency, self.pool, host_store, out.c(),
+                                              scratch, scratch.numel(), y, stream)
         return B.moe_prefill_chunk(self.desc, layer, x.shape[0], plan_cap, x,
                                    self.router[layer], self.bias[layer], self.residency,
                                    self.pool, out.c(), scratch, scratch.numel(), y, stream)

@@ -66,9 +66,11 @@ class PrefillStack:
     layer's input [n_c x H], ``as_[c][l]`` the normalised input,
     ``routes[c][l]`` the routing results and ``ys[c][l]`` the MoE output."""
 
-    def __init__(self, model: DeviceModel, chunks: Sequence[int], plan_cap: int):
+    def __init__(self, model: DeviceModel, chunks: Sequence[int], plan_cap: int,
+                 host_store=None):
         w = model.w
         self.model = model
+        self.host_store = host_store          # missing experts read in place from it
         self.L, self.H = w.n_layers, w.hidden
         self.chunks = list(chunks)
         self.plan_cap = plan_cap
@@ -90,7 +92,7 @@ class PrefillStack:
             B.rl_rmsnorm(n, self.H, x[0], self.as_[c][0], EPS)
             for l in range(self.L):
                 self.model.prefill(l, self.as_[c][l], self.plan_cap, self.routes[c][l],
-                                   self.scratch, self.ys[c][l])
+                                   self.scratch, self.ys[c][l], host_store=self.host_store)
                 B.rl_residual_rmsnorm(n, self.H, x[l], self.ys[c][l], self.routes[c][l].early_out,
                                       x[l + 1], self.as_[c][l + 1], EPS)
             outs.append(x[self.L])

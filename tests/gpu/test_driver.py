@@ -56,3 +56,20 @@ def test_native_driver_equals_python_stack(per_layer, limit, prefetch, sticky):
     assert st["loads"] > 0 and st["early_outs"] > 0
     if prefetch:
         assert st["predictions"] > 0 and st["prefetch_loads"] > 0
+
+
+def test_driver_refuses_after_an_error():
+    """A pool smaller than one layer's selection: the cache refuses the
+    reservation (RL_E_RANGE from the token), and the driver then refuses
+    every further token (RL_E_STATE), since cache and pool may be out of step.
+    The error comes from the host-side cache; no kernel misbehaves."""
+    from quantized_routed_expert_rl_amd import binding as B
+    hot = Workload("serviced", 9, 256, 32, 4, 256, 6, 10, zipf=True, resident=2, popular=True)
+    m = DeviceModel(hot)
+    assert int(m.pool.shape[0]) < hot.top_k
+    nat = NativeServicedDecode(m, HostExpertStore(hot), early_out_limit=0)
+    xs = synth.activations(hot, 2)
+    with pytest.raises(B.RlError, match=r"\(-3\)"):
+        nat.token(to_dev(xs[0]))
+    with pytest.raises(B.RlError, match=r"\(-6\)"):
+        nat.token(to_dev(xs[1]))

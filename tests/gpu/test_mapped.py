@@ -102,3 +102,42 @@ def test_mapped_argument_checks():
                                        store.tensor.data_ptr(), C.byref(out.c()), sc2.data_ptr(),
                                        sc2.numel(), y.data_ptr(), None)
     assert rc == -2                                                # width 64: no matrix-core path
+
+
+@pytest.mark.parametrize("qbits", [2, 3])
+def test_mapped_prefill_chunk_equals_resident_chunk(qbits):
+    hot, full = _workloads(4, qbits)
+    store = HostExpertStore(hot)
+    mh, mf = DeviceModel(hot), DeviceModel(full)
+    T = 70                                          # several passes, a ragged last one
+    x = to_dev(synth.activations(hot, T))
+    sh, sf = mh.prefill_scratch(T), mf.prefill_scratch(T)
+    for l in range(hot.n_layers):
+        oh = RouteBuffers.alloc(T, hot.top_k, hot.n_experts)
+        of = RouteBuffers.alloc(T, hot.top_k, hot.n_experts)
+        yh = torch.full((T, hot.hidden), float("nan"), device="cuda")
+        yf = torch.full((T, hot.hidden), float("nan"), device="cuda")
+        mh.prefill(l, x, hot.plan_cap, oh, sh, yh, host_store=store.tensor)
+        mf.prefill(l, x, hot.plan_cap, of, sf, yf)
+        torch.cuda.synchronize()
+        assert torch.equal(oh.ids, of.ids)
+        assert torch.equal(yh, yf), f"layer {l}"
+        ids = oh.ids.cpu().numpy()
+        assert int(oh.miss_count.cpu()[0]) == int((mh.table[l][ids] < 0).sum()) > 0
+        assert int(oh.early_out.cpu()[0]) == 0
+
+
+def test_mapped_prefill_stack_equals_resident_stack():
+    from quantized_routed_expert_rl_amd.stack import PrefillStack
+    hot, full = _workloads(8)
+    store = HostExpertStore(hot)
+    chunks = (40, 24, 5)
+    x = to_dev(synth.activations(hot, sum(chunks)))
+    ref = PrefillStack(DeviceModel(full), chunks, hot.plan_cap)
+    st = PrefillStack(DeviceModel(hot), chunks, hot.plan_cap, host_store=store.tensor)
+    want = ref.prompt(x)
+    got = st.prompt(x)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    for c in range(len(chunks)):
+        assert torch.equal(st.xs[c], ref.xs[c]), f"chunk {c}"
