@@ -22,12 +22,15 @@ namespace rl {
 // w + 4 take the two halves of K, so two waves share each SIMD and hide each
 // other's LDS and memory latency, and the halves are added in float64 at the
 // end.  Each half runs in 64-value chunks staged through LDS (double buffer;
-// the next chunk's float4 loads are in flight while the current one
-// computes), so each x and W value is read from memory once per block.
-// Inside each 16-value group g of a chunk, MFMA step 4g+i of lane quad kq
-// takes K index 16g + 4kq + i for both operands: one float4 LDS read per
-// lane per group.  Four accumulation chains (one per group) keep the matrix
-// core busy; summed in float64 at the end.
+// a chunk's float4 loads are issued two chunks before it is staged), so each
+// x and W value is read from memory once per block.  Inside each 16-value
+// group g of a chunk, MFMA step 4g+i of lane quad kq takes K index
+// 16g + 4kq + i for both operands: one float4 LDS read per lane per group.
+// A chunk's operands are read into one of two register sets right after the
+// barrier that publishes it, while the previous chunk's MFMAs still run, so
+// the matrix core does not wait for LDS after each barrier.  Four
+// accumulation chains (one per group) keep it busy; summed in float64 at the
+// end.
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr int kRgStride = 68;   // floats per staged row: 64 + 4 keeps float4 reads conflict-free
@@ -73,42 +76,64 @@ __global__ __launch_bounds__(512) void route_gemm_kernel(
   v4d acc4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc4[u] = v4d{0.0, 0.0, 0.0, 0.0};
-  // one chunk: stage its registers into LDS buffer ch&1, refill them with
-  // chunk ch+2, run its MFMAs
-  auto chunk = [&](int ch, float4& a0, float4& a1, float4& b0, float4& b1)
+  auto stage = [&](int ch, const float4& a0, const float4& a1, const float4& b0, const float4& b1)
       __attribute__((always_inline)) {
-    const int buf = ch & 1;
-    float* sa = s_a[kh][buf];
-    float* sb = s_b[kh][buf];
+    float* sa = s_a[kh][ch & 1];
+    float* sb = s_b[kh][ch & 1];
     *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc]) = a0;
     *reinterpret_cast<float4*>(&sa[sr * kRgStride + sc + 4]) = a1;
     *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc]) = b0;
     *reinterpret_cast<float4*>(&sb[sr * kRgStride + sc + 4]) = b1;
-    __syncthreads();
-    if (ch + 2 < nch) fetch(ch + 2, a0, a1, b0, b1);
-    float4 av[4], bv[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      av[g] = *reinterpret_cast<const float4*>(&sa[ra * kRgStride + 16 * g + 4 * kq]);
-      bv[g] = *reinterpret_cast<const float4*>(&sb[rb * kRgStride + 16 * g + 4 * kq]);
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].x), double(bv[g].x), acc4[g], 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].y), double(bv[g].y), acc4[g], 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].z), double(bv[g].z), acc4[g], 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      acc4[g] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(av[g].w), double(bv[g].w), acc4[g], 0, 0, 0);
   };
-  // nch = H/128 is even (H is a multiple of 256), so the register sets alternate in a fixed order
+  // operand registers of one chunk: group g of A and B
+  float4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3;
+  auto readop = [&](int ch, float4& a0, float4& a1, float4& a2, float4& a3, float4& b0, float4& b1,
+                    float4& b2, float4& b3) __attribute__((always_inline)) {
+    const float* sa = s_a[kh][ch & 1] + ra * kRgStride + 4 * kq;
+    const float* sb = s_b[kh][ch & 1] + rb * kRgStride + 4 * kq;
+    a0 = *reinterpret_cast<const float4*>(sa);
+    a1 = *reinterpret_cast<const float4*>(sa + 16);
+    a2 = *reinterpret_cast<const float4*>(sa + 32);
+    a3 = *reinterpret_cast<const float4*>(sa + 48);
+    b0 = *reinterpret_cast<const float4*>(sb);
+    b1 = *reinterpret_cast<const float4*>(sb + 16);
+    b2 = *reinterpret_cast<const float4*>(sb + 32);
+    b3 = *reinterpret_cast<const float4*>(sb + 48);
+  };
+  auto mma = [&](const float4& a0, const float4& a1, const float4& a2, const float4& a3,
+                 const float4& b0, const float4& b1, const float4& b2, const float4& b3)
+      __attribute__((always_inline)) {
+#define RG_STEP(c)                                                                                  \
+    acc4[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a0.c), double(b0.c), acc4[0], 0, 0, 0); \
+    acc4[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a1.c), double(b1.c), acc4[1], 0, 0, 0); \
+    acc4[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a2.c), double(b2.c), acc4[2], 0, 0, 0); \
+    acc4[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a3.c), double(b3.c), acc4[3], 0, 0, 0);
+    RG_STEP(x) RG_STEP(y) RG_STEP(z) RG_STEP(w)
+#undef RG_STEP
+  };
+  // chunk ch's MFMAs are issued around the barrier that publishes chunk
+  // ch+1, and chunk ch+1's operands are read while they run.  nch = H/128 is
+  // even (H is a multiple of 256), so the register sets alternate in a fixed
+  // order.
+  stage(0, pa0, pa1, pb0, pb1);
+  if (2 < nch) fetch(2, pa0, pa1, pb0, pb1);
+  __syncthreads();
+  readop(0, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
   for (int ch = 0; ch < nch; ch += 2) {
-    chunk(ch, pa0, pa1, pb0, pb1);
-    chunk(ch + 1, qa0, qa1, qb0, qb1);
+    // even chunk ch: operands in x; chunk ch+1's staged values in q
+    stage(ch + 1, qa0, qa1, qb0, qb1);
+    if (ch + 3 < nch) fetch(ch + 3, qa0, qa1, qb0, qb1);
+    mma(xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
+    __syncthreads();
+    readop(ch + 1, ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3);
+    // odd chunk ch+1: operands in y; chunk ch+2's staged values in p
+    if (ch + 2 < nch) {
+      stage(ch + 2, pa0, pa1, pb0, pb1);
+      if (ch + 4 < nch) fetch(ch + 4, pa0, pa1, pb0, pb1);
+    }
+    mma(ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3);
+    __syncthreads();
+    if (ch + 2 < nch) readop(ch + 2, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
   }
   v4d acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   if (kh == 1) s_part[wv][l] = acc;
