@@ -30,7 +30,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=256, help="decode calls per step")
-    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=100,
+                    help="untimed back-to-back chunks before the prefill timings (about 25 ms: "
+                         "the chunk time settles only after some tens of milliseconds of load)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
@@ -293,7 +296,7 @@ def main():
             m3.prefill(0, X3, w3.plan_cap, r3, s3, Y3)
 
         with torch.cuda.stream(stream):
-            for _ in range(2):
+            for _ in range(max(2, args.prefill_warmup)):
                 chunk()
             stream.synchronize()
             p_eager_ms = event_ms(chunk, stream, args.prefill_reps)
