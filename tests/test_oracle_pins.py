@@ -13,43 +13,23 @@ import pytest
 import scipy.special
 
 import brute
+from blockfmt import exact_weight, pack_tensor, pack_tensor_fast
 from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import synth, workloads
 
 
-# ---------------------------------------------------------------- helpers
-def pack_tensor(codes, scales, d, qbits):
-    """Write a block-format tensor from explicit fields, byte by byte, at the
-    positions the format defines (independent of every other packer)."""
-    codes = np.asarray(codes, np.int64).reshape(-1)
-    nb = codes.size // 256
-    up = lambda n: -(-n // 256) * 256
-    q_end = nb * 64
-    hb_off = up(q_end) if qbits == 3 else None
-    s_off = up(hb_off + nb * 32) if qbits == 3 else up(q_end)
-    d_off = up(s_off + nb * 4)
-    buf = np.zeros(up(d_off + nb * 2), np.uint8)
-    for f, c in enumerate(codes):
-        b, j = divmod(f, 256)
-        buf[64 * b + j // 4] |= (int(c) & 3) << (2 * (j % 4))
-        if qbits == 3:
-            buf[hb_off + 32 * b + j // 8] |= ((int(c) >> 2) & 1) << (j % 8)
-    scales = np.asarray(scales, np.int64).reshape(nb, 8)
-    for b in range(nb):
-        for g in range(8):
-            buf[s_off + 4 * b + g // 2] |= int(scales[b, g]) << (4 * (g % 2))
-    dh = np.asarray(d, np.float16).reshape(nb)
-    buf[d_off:d_off + 2 * nb] = dh.view(np.uint8)
-    return buf
-
-
-def exact_weight(c, s, d, qbits):
-    if qbits == 2:
-        return Fraction(d) * (2 * s + 1) * (2 * c - 3) / 32
-    return Fraction(d) * (2 * s + 1) * (2 * c - 7) / 64
-
-
 # ---------------------------------------------------------- block format
+@pytest.mark.parametrize("qbits", [2, 3])
+def test_fast_packer_writes_the_same_bytes(qbits):
+    rng = np.random.default_rng(qbits)
+    n = 256 * 6
+    codes = rng.integers(0, 4 << (qbits - 2), n)
+    scales = rng.integers(0, 16, (n // 256, 8))
+    d = rng.uniform(0.01, 2.0, n // 256)
+    assert np.array_equal(pack_tensor_fast(codes, scales, d, qbits),
+                          pack_tensor(codes, scales, d, qbits))
+
+
 def test_byte_counts():
     assert O.block_layout(512 * 2048, 2)["total"] == 286_720       # 70 B/block
     assert O.block_layout(512 * 2048, 3)["total"] == 417_792       # 102 B/block
