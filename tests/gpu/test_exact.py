@@ -31,6 +31,7 @@ from blockfmt import pack_tensor_fast
 from gpu.common import check_route
 from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import binding as B
+from quantized_routed_expert_rl_amd import synth
 from quantized_routed_expert_rl_amd.device import RouteBuffers, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -202,3 +203,43 @@ def _prefill_exact(H, F, qbits, mapped):
         want = _exact_y(nums, int(r.ids[t][0]), x[t])
         _same_bits(y_ref[t], want, f"oracle token {t}")
         _same_bits(got[t], want, f"prefill {H}x{F} {qbits}-bit token {t}")
+
+
+@pytest.mark.parametrize("path,T", [("route", 1), ("route", 37), ("decode", 1)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_route_logits_exact(path, T, with_bias):
+    """Router logits on a dyadic grid (W in 2^-10 Z with |numerator| <= 2^6,
+    x in 2^-6 Z with |numerator| <= 2^7, bias in 2^-16 Z): every product and
+    partial sum is exact in float64, so each logit is the single float32
+    rounding of the integer sum, to the last bit ("Red Lite dev23", "What
+    changed": the router GEMV in float32 with the sum kept exact), and the
+    ids, slots and flags equal the oracle's.  rl_route takes the float64
+    matrix-core GEMM for any token count; a decode call takes the GEMV."""
+    H, E, k, F = 2048, 64, 8, 256
+    rng = np.random.default_rng(T + 100 * with_bias + 7 * (path == "decode"))
+    nw = rng.integers(-64, 65, (E, H))
+    nx = rng.integers(-128, 129, (T, H))
+    W = (nw / 1024).astype(np.float32)
+    x = (nx / 64).astype(np.float32)
+    nb = rng.integers(-2 ** 20, 2 ** 20, E) if with_bias else np.zeros(E, np.int64)
+    bias = (nb / 65536).astype(np.float32) if with_bias else None
+    table = np.arange(E, dtype=np.int32)[None, :]
+    want = ((nx @ nw.T + nb[None, :]).astype(np.float64) / 65536).astype(np.float32)
+    d = B.desc(H, E, k, F, 1, 2, E)
+    out = RouteBuffers.alloc(T, k, E)
+    bd = None if bias is None else to_dev(bias)
+    if path == "route":
+        scratch = torch.zeros(B.rl_route_scratch_bytes(d, T), dtype=torch.uint8, device="cuda")
+        B.rl_route(d, 0, T, to_dev(x), to_dev(W), bd, to_dev(table), out.c(), scratch,
+                   scratch.numel())
+    else:
+        pool = to_dev(np.stack([np.concatenate([synth.random_tensor(rng, H * F, 2)
+                                                for _ in range(3)]) for _ in range(E)]))
+        scratch = torch.zeros(B.rl_decode_scratch_bytes(d), dtype=torch.uint8, device="cuda")
+        y = torch.empty(H, device="cuda")
+        B.moe_decode_layer(d, 0, to_dev(x), to_dev(W), bd, to_dev(table), pool, out.c(),
+                           scratch, scratch.numel(), y)
+    r = O.route(x, W, bias, table[0], k)
+    check_route(out, r)
+    _same_bits(r.logits, want, "oracle logits")
+    _same_bits(out.logits.cpu().numpy(), want, f"{path} logits T={T}")
