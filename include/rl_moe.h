@@ -23,8 +23,12 @@
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
  *     and owns every buffer and keeps it alive until the work queued on
  *     `stream` has finished.
- *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
- *     enqueues work on it: no allocation, no free, no synchronisation.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call of the
+ *     layer API only enqueues work on it: no allocation, no free, no
+ *     synchronisation.  The exceptions are the host objects at the end: the
+ *     expert cache (rl_cache_*, host memory only, no stream) and the decode
+ *     driver (rl_driver_*, which allocates at creation and waits for its
+ *     stream at the end of each token).
  *   - Arguments are validated on the host before anything is enqueued; a
  *     negative return code means nothing was enqueued.  RL_E_DEVICE means a
  *     launch failed (hipGetLastError) and the queued state is unspecified.
