@@ -179,6 +179,29 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x,
                      const rl_route_out* route, void* scratch,
                      int64_t scratch_bytes, float* y, void* stream);
 
+/* moe_decode_layer preceded by the step between two layers of a stack (a
+ * pre-norm decoder: each layer's input is the RMSNorm of the residual
+ * stream, and the layer's output is added to the stream), with that step
+ * done inside the layer's first kernel instead of a launch of its own:
+ *   r = x_prev + y_prev, or x_prev when y_prev is NULL or *flag_prev is set
+ *       (the previous layer stopped: its y is not valid), in float32;
+ *   a = r / sqrt(mean(r^2) + eps), mean of squares in float64;
+ *   then moe_decode_layer(d, layer, a, ...).
+ * x_prev, y_prev [H] float32 (y_prev may be NULL); flag_prev: the previous
+ * layer's early-out word (may be NULL: never set); x_out [H] receives r (NULL:
+ * not written); a_out [H] receives a (required).  The results are bit-identical
+ * to rl_residual_rmsnorm (or rl_rmsnorm when y_prev is NULL) followed by
+ * moe_decode_layer on a_out.  x_out and a_out must not overlap each other,
+ * x_prev or y_prev (RL_E_INVAL); eps must be finite and >= 0 (RL_E_RANGE).
+ * With RL_STICKY_EARLY_OUT and the shared flag set, r and a are still
+ * written and the layer does nothing else. */
+int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_prev,
+                           const float* y_prev, const uint32_t* flag_prev, float eps,
+                           float* x_out, float* a_out, const float* router_w,
+                           const float* router_bias, const int32_t* residency,
+                           const void* slot_pool, const rl_route_out* route, void* scratch,
+                           int64_t scratch_bytes, float* y, void* stream);
+
 /* moe_decode_layer with in-place reads of missing experts: a selected expert
  * that is not resident is read where it lies in `host_store` (pinned, mapped
  * host memory holding every expert of every layer: row layer * E + expert,

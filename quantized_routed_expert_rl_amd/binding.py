@@ -57,6 +57,11 @@ _SIGS = {
     "moe_decode_layer": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RlRouteOut),
                                    C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "moe_decode_layer_after": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.POINTER(RlRouteOut), C.c_void_p, C.c_int64,
+                                         C.c_void_p, C.c_void_p]),
     "moe_decode_layer_mapped": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                           C.c_void_p, C.POINTER(RlRouteOut), C.c_void_p,
@@ -199,6 +204,17 @@ def moe_decode_layer(d, layer, x, router_w, router_bias, residency, slot_pool,
                                       _ptr(router_bias), _ptr(residency), _ptr(slot_pool),
                                       C.byref(route), _ptr(scratch), scratch_bytes, _ptr(y),
                                       _stream(stream)), "moe_decode_layer")
+
+
+def moe_decode_layer_after(d, layer, x_prev, y_prev, flag_prev, eps, x_out, a_out, router_w,
+                           router_bias, residency, slot_pool, route: RlRouteOut, scratch,
+                           scratch_bytes, y, stream=None) -> int:
+    return check(lib.moe_decode_layer_after(C.byref(d), layer, _ptr(x_prev), _ptr(y_prev),
+                                            _ptr(flag_prev), eps, _ptr(x_out), _ptr(a_out),
+                                            _ptr(router_w), _ptr(router_bias), _ptr(residency),
+                                            _ptr(slot_pool), C.byref(route), _ptr(scratch),
+                                            scratch_bytes, _ptr(y), _stream(stream)),
+                 "moe_decode_layer_after")
 
 
 def moe_decode_layer_mapped(d, layer, x, router_w, router_bias, residency, slot_pool, host_store,

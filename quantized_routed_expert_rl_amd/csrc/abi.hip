@@ -299,6 +299,41 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x, const 
   return launch_status();
 }
 
+int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_prev,
+                           const float* y_prev, const uint32_t* flag_prev, float eps,
+                           float* x_out, float* a_out, const float* router_w,
+                           const float* router_bias, const int32_t* residency,
+                           const void* slot_pool, const rl_route_out* route, void* scratch,
+                           int64_t scratch_bytes, float* y, void* stream) {
+  int rc = check_common(d, layer, x_prev, router_w, residency, route, scratch);
+  if (rc) return rc;
+  if (!slot_pool || !y || !a_out || !aligned(slot_pool, 256) || !aligned(y, 16) ||
+      !aligned(a_out, 16) || (y_prev && !aligned(y_prev, 16)) || (x_out && !aligned(x_out, 16)))
+    return RL_E_INVAL;
+  // the router's blocks read x_prev and y_prev while block 0 writes x_out and a_out
+  const void* outs[2] = {x_out, a_out};
+  for (const void* o : outs)
+    if (o && (o == x_prev || o == y_prev)) return RL_E_INVAL;
+  if (x_out && x_out == a_out) return RL_E_INVAL;
+  if (!(eps >= 0.f) || !(eps < 3.0e38f)) return RL_E_RANGE;
+  const DecodeLayout l = decode_layout(d, 1);
+  if (scratch_bytes < l.total) return RL_E_SCRATCH;
+  uint8_t* s = static_cast<uint8_t*>(scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeArgs da = decode_args(d, layer, a_out, router_w, router_bias, residency, slot_pool, route,
+                              s, l, y);
+  da.x_prev = x_prev;
+  da.y_prev = y_prev;
+  da.flag_prev = flag_prev;
+  da.x_out = x_out;
+  da.a_out = a_out;
+  da.eps = eps;
+  launch_decode_router(da, st);
+  launch_decode_gateup(da, st);
+  launch_decode_down_sum(da, st);
+  return launch_status();
+}
+
 int moe_decode_layer_mapped(const rl_moe_desc* d, int32_t layer, const float* x,
                             const float* router_w, const float* router_bias,
                             const int32_t* residency, const void* slot_pool,

@@ -83,6 +83,85 @@ __global__ __launch_bounds__(64) void decode_router_kernel(
   }
 }
 
+// The step between two layers of a stack folded into the router: each block
+// (one wave) rebuilds r = x_prev + y_prev (x_prev when there is no y_prev or
+// the previous layer's flag is set) and a = rmsnorm(r) with the arithmetic of
+// residual_rmsnorm_kernel: thread t of that 256-thread kernel owns elements
+// t + 256u and chains their float64 squares in u order; here lane l runs the
+// chains of threads l + 64w (w = 0..3), the same butterfly sum gives each
+// wave's total, and the four totals are added in w order, so a is
+// bit-identical to that kernel's.  Block 0 writes r and a; every block then
+// computes its router row as decode_router_kernel does, from a staged in LDS.
+template <int NM>
+__global__ __launch_bounds__(64) void decode_router_residual_kernel(
+    const float* __restrict__ x_prev, const float* __restrict__ y_prev,
+    const uint32_t* __restrict__ flag_prev, float* __restrict__ x_out, float* __restrict__ a_out,
+    float eps, const float* __restrict__ W, const float* __restrict__ bias, int E, int H,
+    float* __restrict__ logits, float* __restrict__ logits_out,
+    const uint32_t* __restrict__ early_out, int sticky) {
+  __shared__ __align__(16) float s_a[256 * NM];
+  const int lane = threadIdx.x;
+  const int e = blockIdx.x;
+  if (e > 0 && sticky && *early_out) return;      // block 0 still writes r and a
+  float4 wv[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+    wv[m] = *reinterpret_cast<const float4*>(W + int64_t(e) * H + 256 * m + 4 * lane);
+  const bool skip = !y_prev || (flag_prev && *flag_prev);
+  float v[4][NM];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+      const int i = lane + 64 * w + 256 * u;
+      v[w][u] = skip ? x_prev[i] : x_prev[i] + y_prev[i];
+    }
+  double tot[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+      const double d = v[w][u];
+      s = fma(d, d, s);
+    }
+    tot[w] = wave_sum_f64(s);
+  }
+  const double inv = 1.0 / sqrt((tot[0] + tot[1] + tot[2] + tot[3]) / H + double(eps));
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+      const int i = lane + 64 * w + 256 * u;
+      const float av = float(double(v[w][u]) * inv);
+      s_a[i] = av;
+      if (e == 0) {
+        if (x_out) x_out[i] = v[w][u];
+        a_out[i] = av;
+      }
+    }
+  if (sticky && *early_out) return;
+  wave_lds_sync();
+  float4 xv[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) xv[m] = *reinterpret_cast<const float4*>(&s_a[256 * m + 4 * lane]);
+  double acc = 0.0;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    acc = fma(double(wv[m].x), double(xv[m].x), acc);
+    acc = fma(double(wv[m].y), double(xv[m].y), acc);
+    acc = fma(double(wv[m].z), double(xv[m].z), acc);
+    acc = fma(double(wv[m].w), double(xv[m].w), acc);
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) {
+    if (bias) acc += double(bias[e]);
+    const float l = float(acc);
+    logits[e] = l;
+    if (logits_out) logits_out[e] = l;
+  }
+}
+
 // -------------------------------------------------- 2. top-k + gate/up
 // Block = (expert rank r, 16 rows j); wave w takes rows j0+4w .. +3 of gate
 // and of up.  Wave 0 selects the experts while the other waves load x;
@@ -219,7 +298,22 @@ static void router_rpb(const DecodeArgs& a, int rows, hipStream_t st) {
 
 // One row per single-wave block (E <= 1024 blocks): with two rows per wave
 // the token took 0.1 us longer at E = 512.
-void launch_decode_router(const DecodeArgs& a, hipStream_t st) { router_rpb<1>(a, 1, st); }
+void launch_decode_router(const DecodeArgs& a, hipStream_t st) {
+  if (!a.a_out) {
+    router_rpb<1>(a, 1, st);
+    return;
+  }
+  switch (a.H) {
+#define RL_CASE(NM)                                                                            \
+  case 256 * NM:                                                                               \
+    decode_router_residual_kernel<NM><<<a.E, 64, 0, st>>>(                                     \
+        a.x_prev, a.y_prev, a.flag_prev, a.x_out, a.a_out, a.eps, a.W, a.bias, a.E, a.H,       \
+        a.logits, a.logits_out, a.early_out, int(a.sticky));                                   \
+    break;
+    RL_CASE(1) RL_CASE(2) RL_CASE(4) RL_CASE(8)
+#undef RL_CASE
+  }
+}
 
 template <int N, int QBITS, int LPR>
 static void gateup_l(const DecodeArgs& a, hipStream_t st) {

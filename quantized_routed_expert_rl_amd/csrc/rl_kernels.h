@@ -47,6 +47,16 @@ struct DecodeArgs {
   // memory at host + expert * slot_bytes (device-visible address), and the
   // flag stays clear; NULL = early-out on a miss
   const uint8_t* host = nullptr;
+  // the step before the layer, folded into the router kernel (a_out NULL:
+  // none, x is the layer input): r = x_prev + y_prev (x_prev alone when
+  // y_prev is NULL or *flag_prev is set), written to x_out when not NULL;
+  // x = a_out = rmsnorm(r) with epsilon eps
+  const float* x_prev = nullptr;
+  const float* y_prev = nullptr;
+  const uint32_t* flag_prev = nullptr;
+  float* x_out = nullptr;
+  float* a_out = nullptr;
+  float eps = 0.f;
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);

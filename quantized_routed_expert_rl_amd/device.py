@@ -102,6 +102,15 @@ class DeviceModel:
                                   self.residency, self.pool, out.c(), scratch, scratch.numel(),
                                   y, stream)
 
+    def decode_after(self, layer, x_prev, y_prev, flag_prev, eps, x_out, a_out,
+                     out: RouteBuffers, scratch, y, stream=None, desc=None):
+        """The step between two stack layers (residual add, RMSNorm) folded
+        into this layer's decode call (moe_decode_layer_after)."""
+        return B.moe_decode_layer_after(desc or self.desc, layer, x_prev, y_prev, flag_prev, eps,
+                                        x_out, a_out, self.router[layer], self.bias[layer],
+                                        self.residency, self.pool, out.c(), scratch,
+                                        scratch.numel(), y, stream)
+
     def prefill(self, layer, x, plan_cap, out: RouteBuffers, scratch, y, stream=None,
                 host_store=None):
         if host_store is not None:            # missing experts read in place

@@ -8,9 +8,11 @@ kernel downstream of a flagged layer returns at once).  The norm, the MoE
 layer and the residual add all run in librlmoe's kernels; PyTorch only holds
 the buffers.  Between two layers one launch (rl_residual_rmsnorm) writes
 x_{l+1} and a_{l+1}, so a layer costs its three (decode) MoE launches plus
-one, and every layer's input stays available for checking.
+one, and every layer's input stays available for checking; single-token
+decode folds that step into the next layer's first kernel instead
+(moe_decode_layer_after), so a layer costs its three launches.
 
-``DecodeStack`` runs single tokens through ``moe_decode_layer``;
+``DecodeStack`` runs single tokens through ``moe_decode_layer_after``;
 ``PrefillStack`` runs a prompt chunk by chunk through ``moe_prefill_chunk``
 ("Red Lite dev20 - batched prompt ingestion", "What changed": chunks of the
 prompt go through every layer in turn).
@@ -49,8 +51,24 @@ class DecodeStack:
         self.scratch = model.decode_scratch()
 
     def token(self, x0: torch.Tensor) -> torch.Tensor:
-        """Runs x0 [H] (device) through the stack on the current stream."""
+        """Runs x0 [H] (device) through the stack on the current stream.
+        Without a host store each layer's call also does the step before it
+        (the previous layer's residual add and this layer's RMSNorm) in its
+        first kernel (moe_decode_layer_after), one launch less per layer, with
+        the same bits as the separate launch."""
         self.x[0].copy_(x0.reshape(self.H))
+        if self.host_store is None:
+            for l in range(self.L):
+                first = l == 0
+                self.model.decode_after(
+                    l, self.x[0] if first else self.x[l - 1], None if first else self.y[l - 1],
+                    None if first else self.routes[l - 1].early_out, EPS,
+                    None if first else self.x[l], self.a[l], self.routes[l], self.scratch,
+                    self.y[l])
+            l = self.L - 1
+            B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
+                                  self.x[l + 1], self.a[l + 1], EPS)
+            return self.x[self.L]
         B.rl_rmsnorm(1, self.H, self.x[0], self.a[0], EPS)
         for l in range(self.L):
             self.model.decode(l, self.a[l], self.routes[l], self.scratch, self.y[l],

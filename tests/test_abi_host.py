@@ -107,6 +107,28 @@ def test_errors_before_any_launch():
     assert B.lib.rl_strerror(B.RL_E_SCRATCH).decode() == "scratch buffer too small"
 
 
+def test_decode_after_argument_checks():
+    d = B.desc(2048, 512, 10, 512, 2, 2, 512)
+    out = B.route_out(0x100, 0x100, 0x100, 0x100, 0x100)
+    sb = B.rl_decode_scratch_bytes(d)
+
+    def call(x_prev=0x1000, y_prev=0x2000, flag=0x100, eps=1e-6, x_out=0x3000, a_out=0x4000,
+             pool=0x1000, nbytes=sb):
+        return B.lib.moe_decode_layer_after(C.byref(d), 0, x_prev, y_prev, flag, eps, x_out, a_out,
+                                            0x1000, None, 0x1000, pool, C.byref(out), 0x1000,
+                                            nbytes, 0x5000, None)
+    assert call(a_out=None) == B.RL_E_INVAL                     # a_out is required
+    assert call(x_out=0x1000) == B.RL_E_INVAL                   # r over x_prev
+    assert call(a_out=0x2000) == B.RL_E_INVAL                   # a over y_prev
+    assert call(x_out=0x4000) == B.RL_E_INVAL                   # r over a
+    assert call(x_out=0x3004) == B.RL_E_INVAL                   # misaligned
+    assert call(y_prev=0x2008) == B.RL_E_INVAL
+    assert call(pool=None) == B.RL_E_INVAL
+    assert call(eps=-1.0) == B.RL_E_RANGE
+    assert call(eps=float("nan")) == B.RL_E_RANGE
+    assert call(nbytes=sb - 1) == B.RL_E_SCRATCH
+
+
 def test_driver_argument_checks():
     """The decode driver's entry points reject missing arguments before any
     device work (no GPU needed)."""
