@@ -6,6 +6,7 @@
 //
 // The int8 operands and their exactness are described in rl_mfma.h; columns
 // of the B operand are 4 * token + digit.
+#include <atomic>
 #include <type_traits>
 
 #include "rl_common.h"
@@ -420,19 +421,20 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
 }
 
 // Compute units of the current device (the expert kernels run one block per
-// compute unit); queried once per device.
+// compute unit); queried once per device.  Calls from several host threads
+// may query at the same time; they store the same value.
 static int cu_count() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
