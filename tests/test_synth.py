@@ -72,3 +72,22 @@ def test_pool_places_each_expert_at_its_slot():
         assert np.array_equal(pool[t[0, e]], synth.expert_slot(w, 0, e))
     part = synth.fill_slots(w, t, 4, 3)
     assert np.array_equal(part, pool[4:7])
+
+
+def test_real_shapes_match_the_figures_the_notes_print():
+    """The real-shape workloads use the layer and chunk shape the notes print
+    (tests/golden/layer_shape.txt, each figure with its page and section)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "layer_shape.txt")
+    fig = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            name, value = line.split()[:2]
+            fig[name] = int(value)
+    for name in ("decode_1l", "decode_48l", "decode_48l_hot", "prefill_1l"):
+        w = workloads.get(name)
+        assert (w.hidden, w.width, w.top_k) == (fig["hidden"], fig["width"], fig["top_k"]), name
+    p = workloads.get("prefill_1l")
+    assert p.tokens == fig["prefill_chunk"] and p.plan_cap == fig["plan_cap"]
+    p48 = workloads.get("prefill_48l")
+    assert max(p48.chunks) == fig["prefill_chunk"] and p48.plan_cap == fig["plan_cap"]
