@@ -281,7 +281,10 @@ int rl_prefill_stage(const rl_moe_desc* d, int32_t stage, int32_t layer,
 /* Helpers for stacks of layers (not part of the MoE layer itself).
  * rl_rmsnorm: out[t] = x[t] / sqrt(mean(x[t]^2) + eps), no weight.
  * rl_residual_add: x[t] += y[t], skipped entirely when *early_out != 0
- * (early_out may be NULL = always add).  hidden must be a multiple of 256. */
+ * (early_out may be NULL = always add).  hidden must be a multiple of 256;
+ * the norms take x, out (and y, x_out, a_out below) 16-byte aligned (else
+ * RL_E_INVAL) and accumulate the mean of squares in float64 in a fixed order,
+ * the same in rl_rmsnorm, rl_residual_rmsnorm and moe_decode_layer_after. */
 int rl_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, float* out,
                float eps, void* stream);
 int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,

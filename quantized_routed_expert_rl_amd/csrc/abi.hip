@@ -481,7 +481,7 @@ int rl_prefill_stage(const rl_moe_desc* d, int32_t stage, int32_t layer, int32_t
 
 int rl_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, float* out, float eps,
                void* stream) {
-  if (!x || !out) return RL_E_INVAL;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return RL_E_INVAL;
   if (n_tokens < 1 || hidden < 256 || hidden % 256) return RL_E_RANGE;
   launch_rmsnorm(n_tokens, hidden, x, out, eps, static_cast<hipStream_t>(stream));
   return launch_status();
@@ -498,7 +498,9 @@ int rl_residual_add(int32_t n_tokens, int32_t hidden, float* x, const float* y,
 int rl_residual_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, const float* y,
                         const uint32_t* early_out, float* x_out, float* a_out, float eps,
                         void* stream) {
-  if (!x || !y || !x_out || !a_out) return RL_E_INVAL;
+  if (!x || !y || !x_out || !a_out || !aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16) ||
+      !aligned(a_out, 16))
+    return RL_E_INVAL;
   if (n_tokens < 1 || hidden < 256 || hidden > 2048 || hidden % 256) return RL_E_RANGE;
   launch_residual_rmsnorm(n_tokens, hidden, x, y, early_out, x_out, a_out, eps,
                           static_cast<hipStream_t>(stream));

@@ -85,13 +85,15 @@ __global__ __launch_bounds__(64) void decode_router_kernel(
 
 // The step between two layers of a stack folded into the router: each block
 // (one wave) rebuilds r = x_prev + y_prev (x_prev when there is no y_prev or
-// the previous layer's flag is set) and a = rmsnorm(r) with the arithmetic of
-// residual_rmsnorm_kernel: thread t of that 256-thread kernel owns elements
-// t + 256u and chains their float64 squares in u order; here lane l runs the
-// chains of threads l + 64w (w = 0..3), the same butterfly sum gives each
-// wave's total, and the four totals are added in w order, so a is
-// bit-identical to that kernel's.  Block 0 writes r and a; every block then
-// computes its router row as decode_router_kernel does, from a staged in LDS.
+// the previous layer's flag is set) and a = rmsnorm(r) in the order of the
+// 256-thread norm kernels: there thread t owns the 4-value chunks at
+// 4t + 1024u and chains their float64 squares in (u, component) order; here
+// lane l holds the chunks 256m + 4l of the router's operand layout, which are
+// those of threads l + 64w with m = w + 4u, so chain w runs over m = w, w + 4,
+// ..., the same butterfly sum gives each wave's total and the four totals
+// are added in w order: a is bit-identical to rl_residual_rmsnorm's.  Block
+// 0 writes r and a; every block then computes its router row as
+// decode_router_kernel does, from the same registers.
 template <int NM>
 __global__ __launch_bounds__(64) void decode_router_residual_kernel(
     const float* __restrict__ x_prev, const float* __restrict__ y_prev,
@@ -99,7 +101,6 @@ __global__ __launch_bounds__(64) void decode_router_residual_kernel(
     float eps, const float* __restrict__ W, const float* __restrict__ bias, int E, int H,
     float* __restrict__ logits, float* __restrict__ logits_out,
     const uint32_t* __restrict__ early_out, int sticky) {
-  __shared__ __align__(16) float s_a[256 * NM];
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
   if (e > 0 && sticky && *early_out) return;      // block 0 still writes r and a
@@ -108,43 +109,38 @@ __global__ __launch_bounds__(64) void decode_router_residual_kernel(
   for (int m = 0; m < NM; ++m)
     wv[m] = *reinterpret_cast<const float4*>(W + int64_t(e) * H + 256 * m + 4 * lane);
   const bool skip = !y_prev || (flag_prev && *flag_prev);
-  float v[4][NM];
+  float4 xv[NM];
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int u = 0; u < NM; ++u) {
-      const int i = lane + 64 * w + 256 * u;
-      v[w][u] = skip ? x_prev[i] : x_prev[i] + y_prev[i];
+  for (int m = 0; m < NM; ++m) {
+    const int i = 256 * m + 4 * lane;
+    const float4 xp = *reinterpret_cast<const float4*>(x_prev + i);
+    if (skip) {
+      xv[m] = xp;
+    } else {
+      const float4 yp = *reinterpret_cast<const float4*>(y_prev + i);
+      xv[m] = make_float4(xp.x + yp.x, xp.y + yp.y, xp.z + yp.z, xp.w + yp.w);
     }
+  }
   double tot[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     double s = 0.0;
 #pragma unroll
-    for (int u = 0; u < NM; ++u) {
-      const double d = v[w][u];
-      s = fma(d, d, s);
-    }
+    for (int m = w; m < NM; m += 4) s = chunk_sq(xv[m], s);
     tot[w] = wave_sum_f64(s);
   }
   const double inv = 1.0 / sqrt((tot[0] + tot[1] + tot[2] + tot[3]) / H + double(eps));
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int u = 0; u < NM; ++u) {
-      const int i = lane + 64 * w + 256 * u;
-      const float av = float(double(v[w][u]) * inv);
-      s_a[i] = av;
-      if (e == 0) {
-        if (x_out) x_out[i] = v[w][u];
-        a_out[i] = av;
-      }
+  for (int m = 0; m < NM; ++m) {
+    const int i = 256 * m + 4 * lane;
+    const float4 av = chunk_scale(xv[m], inv);
+    if (e == 0) {
+      if (x_out) *reinterpret_cast<float4*>(x_out + i) = xv[m];
+      *reinterpret_cast<float4*>(a_out + i) = av;
     }
+    xv[m] = av;
+  }
   if (sticky && *early_out) return;
-  wave_lds_sync();
-  float4 xv[NM];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) xv[m] = *reinterpret_cast<const float4*>(&s_a[256 * m + 4 * lane]);
   double acc = 0.0;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {

@@ -139,6 +139,20 @@ __device__ inline float wave_sum_width(float v, int width) {
   return v;
 }
 
+// Float64 sum of squares of a 4-value chunk added to s in component order,
+// and the chunk scaled by inv and rounded to float32 (the RMSNorms).
+__device__ inline double chunk_sq(const float4& f, double s) {
+  s = fma(double(f.x), double(f.x), s);
+  s = fma(double(f.y), double(f.y), s);
+  s = fma(double(f.z), double(f.z), s);
+  return fma(double(f.w), double(f.w), s);
+}
+
+__device__ inline float4 chunk_scale(const float4& f, double inv) {
+  return make_float4(float(double(f.x) * inv), float(double(f.y) * inv), float(double(f.z) * inv),
+                     float(double(f.w) * inv));
+}
+
 __device__ inline double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

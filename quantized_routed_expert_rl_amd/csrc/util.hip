@@ -20,18 +20,23 @@ __device__ inline double block_inv_rms(double s, int H, float eps) {
   return s_inv;
 }
 
+// Element order of the norms: thread t of the 256-thread block owns the
+// 4-value chunks at 4t + 1024u and chains their float64 squares in
+// (u, component) order (chunk_sq); the four waves' sums are added in order.
+// decode_router_residual_kernel repeats this order in one wave (lane l
+// standing for threads l + 64w), so the three norms give the same bits.
 // One block per token: out = x / sqrt(mean(x^2) + eps), the mean of squares
 // accumulated in float64.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* __restrict__ x,
                                                       float* __restrict__ out, float eps) {
   const int64_t base = int64_t(blockIdx.x) * H;
   double s = 0.0;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    const double v = x[base + i];
-    s = fma(v, v, s);
-  }
+  for (int i = 4 * threadIdx.x; i < H; i += 1024)
+    s = chunk_sq(*reinterpret_cast<const float4*>(x + base + i), s);
   const double inv = block_inv_rms(s, H, eps);
-  for (int i = threadIdx.x; i < H; i += 256) out[base + i] = float(double(x[base + i]) * inv);
+  for (int i = 4 * threadIdx.x; i < H; i += 1024)
+    *reinterpret_cast<float4*>(out + base + i) =
+        chunk_scale(*reinterpret_cast<const float4*>(x + base + i), inv);
 }
 
 // The step between two layers of a stack in one launch, one block per token:
@@ -41,26 +46,30 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
     int H, const float* __restrict__ x, const float* __restrict__ y,
     const uint32_t* __restrict__ early_out, float* __restrict__ x_out, float* __restrict__ a_out,
     float eps) {
-  constexpr int kMaxPer = 8;                     // H <= 2048
   const int64_t base = int64_t(blockIdx.x) * H;
   const bool skip = early_out && *early_out;
-  float v[kMaxPer];
+  float4 v[2];
   double s = 0.0;
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int i = threadIdx.x + 256 * u;
+  for (int u = 0; u < 2; ++u) {                  // H <= 2048
+    const int i = 4 * threadIdx.x + 1024 * u;
     if (i < H) {
-      v[u] = skip ? x[base + i] : x[base + i] + y[base + i];
-      x_out[base + i] = v[u];
-      const double d = v[u];
-      s = fma(d, d, s);
+      const float4 xv = *reinterpret_cast<const float4*>(x + base + i);
+      if (skip) {
+        v[u] = xv;
+      } else {
+        const float4 yv = *reinterpret_cast<const float4*>(y + base + i);
+        v[u] = make_float4(xv.x + yv.x, xv.y + yv.y, xv.z + yv.z, xv.w + yv.w);
+      }
+      *reinterpret_cast<float4*>(x_out + base + i) = v[u];
+      s = chunk_sq(v[u], s);
     }
   }
   const double inv = block_inv_rms(s, H, eps);
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int i = threadIdx.x + 256 * u;
-    if (i < H) a_out[base + i] = float(double(v[u]) * inv);
+  for (int u = 0; u < 2; ++u) {
+    const int i = 4 * threadIdx.x + 1024 * u;
+    if (i < H) *reinterpret_cast<float4*>(a_out + base + i) = chunk_scale(v[u], inv);
   }
 }
 
