@@ -88,6 +88,9 @@ def test_errors_before_any_launch():
                                  C.byref(out), 0x1000, sp, 0x1000, None)
     assert rc == B.RL_E_SCRATCH                                      # 65 tokens > 64
     assert B.lib.rl_rmsnorm(4, 300, 0x1000, 0x1000, 1e-6, None) == B.RL_E_RANGE
+    assert B.lib.rl_rmsnorm(4, 2048, 0x1004, 0x1000, 1e-6, None) == B.RL_E_INVAL   # misaligned
+    assert B.lib.rl_residual_rmsnorm(1, 2048, 0x1000, 0x1000, None, 0x1008, 0x1000, 1e-6,
+                                     None) == B.RL_E_INVAL
     assert B.lib.rl_residual_add(0, 2048, 0x1000, 0x1000, None, None) == B.RL_E_RANGE
     assert B.lib.rl_residual_rmsnorm(1, 4096, 0x1000, 0x1000, None, 0x1000, 0x1000, 1e-6,
                                      None) == B.RL_E_RANGE              # hidden > 2048
