@@ -489,67 +489,6 @@ def main():
                                else "; token loop in Python")}
             del sv, mh
             torch.cuda.empty_cache()
-        # the same workload with missing experts read in place from the pinned
-        # store (moe_decode_layer_mapped): no layer stops, one graph per token
-        mh = DeviceModel(wh, pool=store.device_pool(synth.residency(wh)))
-        ms = DecodeStack(mh, host_store=store.tensor)
-        xin = torch.empty(wh.hidden, device="cuda")
-        with torch.cuda.stream(stream):
-            xin.copy_(Xh[0])
-            ms.token(xin)
-            gm = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gm, stream=stream):
-                ms.token(xin)
-            stream.synchronize()
-            host_reads = 0
-            for t in range(wh.tokens):           # untimed pass: selections read from host memory
-                xin.copy_(Xh[t])
-                gm.replay()
-                stream.synchronize()
-                host_reads += int(torch.stack([r.miss_count for r in ms.routes]).sum())
-            t0 = time.perf_counter()
-            for t in range(wh.tokens):
-                xin.copy_(Xh[t])
-                gm.replay()
-            stream.synchronize()
-            dt = time.perf_counter() - t0
-        stacks["decode_48l_hot_mapped"] = {
-            "tokens_per_s": round(wh.tokens / dt, 1), "ms_per_token": round(dt * 1e3 / wh.tokens, 3),
-            "host_reads_per_token": round(host_reads / wh.tokens, 2),
-            "run_time_hit_rate": round(1 - host_reads / (wh.tokens * wh.n_layers * wh.top_k), 4),
-            "workload": f"{wh.tokens} sequential tokens through 48 decode layers, Zipf-biased routing, "
-                        "10752 slots seeded with each layer's 224 most popular experts, missing "
-                        "experts read in place from pinned host memory by the kernels; one HIP graph "
-                        "per token"}
-        del ms, mh
-        torch.cuda.empty_cache()
-        # the 1100-token prompt through the same bounded pool, misses read in
-        # place (moe_prefill_chunk_mapped); same experts as the store above
-        wph = workloads.get("prefill_48l_hot")
-        assert (wph.wid, wph.resident, wph.popular) == (wh.wid, wh.resident, wh.popular)
-        mph = DeviceModel(wph, pool=store.device_pool(synth.residency(wph)))
-        psh = PrefillStack(mph, wph.chunks, wph.plan_cap, host_store=store.tensor)
-        Xph = to_dev(synth.activations(wph, wph.tokens))
-        with torch.cuda.stream(stream):
-            psh.prompt(Xph)
-            stream.synchronize()
-            misses = sum(int(r.miss_count.cpu()[0]) for rs in psh.routes for r in rs)
-            reps = 2
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                psh.prompt(Xph)
-            stream.synchronize()
-            dt = (time.perf_counter() - t0) / reps
-        pairs = wph.tokens * wph.n_layers * wph.top_k
-        stacks["prefill_48l_hot_mapped"] = {
-            "prompt_tokens_per_s": round(wph.tokens / dt, 1), "ms_per_prompt": round(dt * 1e3, 3),
-            "host_read_pairs": misses, "run_time_hit_rate": round(1 - misses / pairs, 4),
-            "workload": f"{wph.tokens}-token prompt in chunks 512/512/76 through 48 prefill layers, "
-                        "Zipf-biased routing, 10752 slots holding each layer's 224 most popular "
-                        "experts, missing experts read in place from pinned host memory by the "
-                        "expert kernels (once per pass of their tokens)"}
-        del psh, mph
-        torch.cuda.empty_cache()
         del store
         line["stacks"] = stacks
 

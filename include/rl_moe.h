@@ -191,8 +191,9 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x,
  * layer's early-out word (may be NULL: never set); x_out [H] receives r (NULL:
  * not written); a_out [H] receives a (required).  The results are bit-identical
  * to rl_residual_rmsnorm (or rl_rmsnorm when y_prev is NULL) followed by
- * moe_decode_layer on a_out.  x_out and a_out must not overlap each other,
- * x_prev or y_prev (RL_E_INVAL); eps must be finite and >= 0 (RL_E_RANGE).
+ * moe_decode_layer on a_out.  The hidden floats of x_out and of a_out must
+ * not share a byte with each other, x_prev or y_prev (RL_E_INVAL; nothing is
+ * enqueued); eps must be finite and >= 0 (RL_E_RANGE).
  * With RL_STICKY_EARLY_OUT and the shared flag set, r and a are still
  * written and the layer does nothing else. */
 int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_prev,
@@ -201,26 +202,6 @@ int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_p
                            const float* router_bias, const int32_t* residency,
                            const void* slot_pool, const rl_route_out* route, void* scratch,
                            int64_t scratch_bytes, float* y, void* stream);
-
-/* moe_decode_layer with in-place reads of missing experts: a selected expert
- * that is not resident is read where it lies in `host_store` (pinned, mapped
- * host memory holding every expert of every layer: row layer * E + expert,
- * rl_slot_bytes each, 256-byte aligned), by the same kernels over PCIe,
- * instead of stopping the layer.  The notes load misses into GPU-visible
- * buffers before running them, and tried reading experts in place from a
- * mapping as an option ("Red Lite dev20 - batched prompt ingestion", expert
- * kernel layout: numerically identical, slower on their machine); here the
- * pinned store is read directly, so a token needs no host round trip.
- * miss_count still counts the selections served from host memory; the flag
- * stays 0 and y is always written.  Matrix-core shapes only (width a
- * multiple of 256: else RL_E_SHAPE); RL_E_INVAL for a NULL or misaligned
- * host_store, one the device cannot map (hipHostGetDevicePointer fails), or
- * RL_STICKY_EARLY_OUT in the descriptor. */
-int moe_decode_layer_mapped(const rl_moe_desc* d, int32_t layer, const float* x,
-                            const float* router_w, const float* router_bias,
-                            const int32_t* residency, const void* slot_pool,
-                            const void* host_store, const rl_route_out* route, void* scratch,
-                            int64_t scratch_bytes, float* y, void* stream);
 
 /* One prefill chunk of n_tokens tokens through layer `layer` (dev20 "What
  * changed"): route every token, build the chunk's plan -- consecutive token
@@ -238,22 +219,6 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
                       const void* slot_pool, const rl_route_out* route,
                       void* scratch, int64_t scratch_bytes, float* y,
                       void* stream);
-
-/* moe_prefill_chunk with in-place reads of missing experts: a bucket whose
- * expert is not resident is read by the expert kernels where it lies in
- * `host_store` (pinned, mapped host memory holding every expert of every
- * layer: row layer * E + expert, rl_slot_bytes each, 256-byte aligned),
- * once per pass of its tokens, instead of stopping the chunk (the notes'
- * optional in-place reading, "Red Lite dev20 - batched prompt ingestion",
- * expert kernel layout).  miss_count still counts the selections served
- * from host memory; the flag stays 0 and y is always written.  Same shapes
- * and errors as moe_decode_layer_mapped (matrix-core shapes only). */
-int moe_prefill_chunk_mapped(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
-                             int32_t plan_cap, const float* x, const float* router_w,
-                             const float* router_bias, const int32_t* residency,
-                             const void* slot_pool, const void* host_store,
-                             const rl_route_out* route, void* scratch, int64_t scratch_bytes,
-                             float* y, void* stream);
 
 /* Stage entry points, for tests and benchmarks: each enqueues the kernels of
  * one step of a path above, with the same arguments and scratch layout.

@@ -333,13 +333,16 @@ def pair_plan(ids: np.ndarray, n_experts: int, plan_cap: int) -> Plan:
 
 def prefill_chunk(shape: LayerShape, x: np.ndarray, w_router, bias,
                   residency_row, read_slot: SlotReader, plan_cap: int,
-                  tokens: Optional[List[int]] = None):
+                  tokens: Optional[List[int]] = None, map_fn=map):
     """One prefill chunk of T tokens through the routed FFN ([dev20]).
 
     Returns (route, plan, y).  The chunk's flag is raised by any miss among
     its T*k selections; then plan and y are None.  ``tokens`` restricts y to
     a subset of rows (the others stay NaN) so that a large chunk can be
     checked on a sample; routing and the plan always cover the whole chunk.
+    ``map_fn`` maps the evaluation over the buckets, which are independent of
+    one another (the builtin map by default; a thread pool's map gives the
+    same results sooner).
     """
     r = route(x, w_router, bias, residency_row, shape.top_k)
     if r.early_out:
@@ -347,16 +350,21 @@ def prefill_chunk(shape: LayerShape, x: np.ndarray, w_router, bias,
     plan = pair_plan(r.ids, shape.n_experts, plan_cap)
     T, k = r.ids.shape
     want = set(range(T)) if tokens is None else set(tokens)
-    pair_out = {}
-    for b in range(len(plan.bucket_expert)):
+
+    def bucket_outputs(b):
+        """(pair ids, expert outputs) of bucket b's wanted pairs."""
         ps = [int(p) for p in plan.pairs[plan.bucket_start[b]:plan.bucket_start[b + 1]]
               if int(p) // k in want]
         if not ps:
-            continue
+            return ps, None
         slot = int(r.slots[ps[0] // k, ps[0] % k])
         wg, wu, wd = expert_matrices(read_slot(slot), shape.hidden,
                                      shape.width, shape.qbits)
         _, e = expert_forward(x[[p // k for p in ps]], wg, wu, wd)
+        return ps, e
+
+    pair_out = {}
+    for ps, e in map_fn(bucket_outputs, range(len(plan.bucket_expert))):
         for i, p in enumerate(ps):
             pair_out[p] = e[i]
     y = np.full((T, shape.hidden), np.nan, F32)

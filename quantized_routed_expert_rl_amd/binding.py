@@ -13,7 +13,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("RLMOE_LIB") or os.path.join(_HERE, "librlmoe.so")
 
-RL_OK, RL_E_INVAL, RL_E_SHAPE, RL_E_RANGE, RL_E_SCRATCH, RL_E_DEVICE = 0, -1, -2, -3, -4, -5
+RL_OK, RL_E_INVAL, RL_E_SHAPE, RL_E_RANGE, RL_E_SCRATCH, RL_E_DEVICE, RL_E_STATE = (
+    0, -1, -2, -3, -4, -5, -6)
 
 
 class RlMoeDesc(C.Structure):
@@ -62,18 +63,10 @@ _SIGS = {
                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.POINTER(RlRouteOut), C.c_void_p, C.c_int64,
                                          C.c_void_p, C.c_void_p]),
-    "moe_decode_layer_mapped": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p,
-                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                          C.c_void_p, C.POINTER(RlRouteOut), C.c_void_p,
-                                          C.c_int64, C.c_void_p, C.c_void_p]),
     "moe_prefill_chunk": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
                                     C.c_void_p]),
-    "moe_prefill_chunk_mapped": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
-                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                           C.c_void_p, C.c_void_p, C.POINTER(RlRouteOut),
-                                           C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "rl_decode_stage": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
@@ -215,25 +208,6 @@ def moe_decode_layer_after(d, layer, x_prev, y_prev, flag_prev, eps, x_out, a_ou
                                             _ptr(slot_pool), C.byref(route), _ptr(scratch),
                                             scratch_bytes, _ptr(y), _stream(stream)),
                  "moe_decode_layer_after")
-
-
-def moe_decode_layer_mapped(d, layer, x, router_w, router_bias, residency, slot_pool, host_store,
-                            route: RlRouteOut, scratch, scratch_bytes, y, stream=None) -> int:
-    return check(lib.moe_decode_layer_mapped(C.byref(d), layer, _ptr(x), _ptr(router_w),
-                                             _ptr(router_bias), _ptr(residency), _ptr(slot_pool),
-                                             _ptr(host_store), C.byref(route), _ptr(scratch),
-                                             scratch_bytes, _ptr(y), _stream(stream)),
-                 "moe_decode_layer_mapped")
-
-
-def moe_prefill_chunk_mapped(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,
-                             slot_pool, host_store, route: RlRouteOut, scratch, scratch_bytes, y,
-                             stream=None) -> int:
-    return check(lib.moe_prefill_chunk_mapped(C.byref(d), layer, n_tokens, plan_cap, _ptr(x),
-                                              _ptr(router_w), _ptr(router_bias), _ptr(residency),
-                                              _ptr(slot_pool), _ptr(host_store), C.byref(route),
-                                              _ptr(scratch), scratch_bytes, _ptr(y),
-                                              _stream(stream)), "moe_prefill_chunk_mapped")
 
 
 def moe_prefill_chunk(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,

@@ -30,6 +30,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t a256(int64_t n) { return up256(n); }
 
+// [p, p + bytes) and [q, q + bytes) share a byte (false when either is NULL).
+bool overlap(const void* p, const void* q, int64_t bytes) {
+  if (!p || !q) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + uintptr_t(bytes) && b < a + uintptr_t(bytes);
+}
+
 // --- decode / route scratch: logits [T*E] f32, h [k*F] f32
 struct DecodeLayout {
   int64_t logits, hbuf, total;
@@ -310,11 +317,12 @@ int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_p
   if (!slot_pool || !y || !a_out || !aligned(slot_pool, 256) || !aligned(y, 16) ||
       !aligned(a_out, 16) || (y_prev && !aligned(y_prev, 16)) || (x_out && !aligned(x_out, 16)))
     return RL_E_INVAL;
-  // the router's blocks read x_prev and y_prev while block 0 writes x_out and a_out
-  const void* outs[2] = {x_out, a_out};
-  for (const void* o : outs)
-    if (o && (o == x_prev || o == y_prev)) return RL_E_INVAL;
-  if (x_out && x_out == a_out) return RL_E_INVAL;
+  // the router's blocks read x_prev and y_prev while block 0 writes x_out and
+  // a_out: no byte of an output may lie in another vector
+  const int64_t vb = int64_t(d->hidden) * 4;
+  if (overlap(x_out, a_out, vb) || overlap(x_out, x_prev, vb) || overlap(x_out, y_prev, vb) ||
+      overlap(a_out, x_prev, vb) || overlap(a_out, y_prev, vb))
+    return RL_E_INVAL;
   if (!(eps >= 0.f) || !(eps < 3.0e38f)) return RL_E_RANGE;
   const DecodeLayout l = decode_layout(d, 1);
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
@@ -328,37 +336,6 @@ int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_p
   da.x_out = x_out;
   da.a_out = a_out;
   da.eps = eps;
-  launch_decode_router(da, st);
-  launch_decode_gateup(da, st);
-  launch_decode_down_sum(da, st);
-  return launch_status();
-}
-
-int moe_decode_layer_mapped(const rl_moe_desc* d, int32_t layer, const float* x,
-                            const float* router_w, const float* router_bias,
-                            const int32_t* residency, const void* slot_pool,
-                            const void* host_store, const rl_route_out* route, void* scratch,
-                            int64_t scratch_bytes, float* y, void* stream) {
-  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
-  if (rc) return rc;
-  if (!slot_pool || !y || !host_store || !aligned(slot_pool, 256) || !aligned(y, 16) ||
-      !aligned(host_store, 256) || (d->flags & RL_STICKY_EARLY_OUT))
-    return RL_E_INVAL;
-  if (d->width % 256) return RL_E_SHAPE;            // matrix-core shapes only
-  // the device-visible address of the host store (pinned, mapped memory only)
-  void* dev = nullptr;
-  if (hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0) != hipSuccess || !dev) {
-    (void)hipGetLastError();   // the failed lookup must not surface at the caller's next call
-    return RL_E_INVAL;
-  }
-  const DecodeLayout l = decode_layout(d, 1);
-  if (scratch_bytes < l.total) return RL_E_SCRATCH;
-  uint8_t* s = static_cast<uint8_t*>(scratch);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  DecodeArgs da = decode_args(d, layer, x, router_w, router_bias, residency, slot_pool, route, s,
-                              l, y);
-  if (!da.mfma) return RL_E_SHAPE;
-  da.host = static_cast<const uint8_t*>(dev) + int64_t(layer) * d->n_experts * da.pool.slot_bytes;
   launch_decode_router(da, st);
   launch_decode_gateup(da, st);
   launch_decode_down_sum(da, st);
@@ -383,43 +360,6 @@ int moe_prefill_chunk(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, int
   launch_route(ra, st);
   const PrefillArgs a = prefill_args(d, layer, n_tokens, plan_cap, x, residency, slot_pool, route,
                                      s, l, y);
-  launch_prefill_plan(a, st);
-  launch_prefill_gateup(a, st);
-  launch_prefill_down(a, st);
-  launch_prefill_sum(a, st);
-  return launch_status();
-}
-
-int moe_prefill_chunk_mapped(const rl_moe_desc* d, int32_t layer, int32_t n_tokens,
-                             int32_t plan_cap, const float* x, const float* router_w,
-                             const float* router_bias, const int32_t* residency,
-                             const void* slot_pool, const void* host_store,
-                             const rl_route_out* route, void* scratch, int64_t scratch_bytes,
-                             float* y, void* stream) {
-  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
-  if (rc) return rc;
-  if (!slot_pool || !y || !host_store || !aligned(slot_pool, 256) || !aligned(y, 16) ||
-      !aligned(host_store, 256) || (d->flags & RL_STICKY_EARLY_OUT))
-    return RL_E_INVAL;
-  if (d->width % 256) return RL_E_SHAPE;            // matrix-core shapes only
-  if (n_tokens < 1 || plan_cap < d->top_k) return RL_E_RANGE;
-  void* dev = nullptr;
-  if (hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0) != hipSuccess || !dev) {
-    (void)hipGetLastError();   // the failed lookup must not surface at the caller's next call
-    return RL_E_INVAL;
-  }
-  const PrefillLayout l = prefill_layout(d, n_tokens);
-  if (scratch_bytes < l.total) return RL_E_SCRATCH;
-  uint8_t* s = static_cast<uint8_t*>(scratch);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  RouteArgs ra = route_args(d, layer, n_tokens, x, router_w, router_bias, residency, route,
-                            reinterpret_cast<float*>(s + l.logits));
-  ra.flag_misses = false;                           // misses are read in place
-  launch_route(ra, st);
-  PrefillArgs a = prefill_args(d, layer, n_tokens, plan_cap, x, residency, slot_pool, route, s, l,
-                               y);
-  if (!a.mfma) return RL_E_SHAPE;
-  a.host = static_cast<const uint8_t*>(dev) + int64_t(layer) * d->n_experts * a.pool.slot_bytes;
   launch_prefill_plan(a, st);
   launch_prefill_gateup(a, st);
   launch_prefill_down(a, st);

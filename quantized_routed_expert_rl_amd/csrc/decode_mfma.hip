@@ -130,8 +130,7 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
     const float* __restrict__ x, const float* __restrict__ logits,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
-    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf, int sticky,
-    const uint8_t* __restrict__ host) {
+    uint32_t* miss_count, uint32_t* early_out, float* __restrict__ hbuf, int sticky) {
   if (sticky && *early_out) return;      // a set shared flag stops the whole call
   constexpr int BPT = KB < 4 ? KB : 4;   // K-blocks per tile
   constexpr int RPT = 16 / BPT;          // output rows per tile
@@ -142,7 +141,6 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
   __shared__ float sel_lg[32];
   __shared__ int sel_res[32];
   __shared__ int s_slot[32];
-  __shared__ int s_id[32];
   __shared__ int s_miss;
   __shared__ __align__(16) uint8_t s_xq[KB * 1024];
   __shared__ int s_xe[KB];
@@ -154,17 +152,13 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
       const int miss = finish_token(sel_ids, sel_lg, sel_res, k, E, n_slots, ids, weights, slots);
       if (lane == 0) {
         *miss_count = uint32_t(miss);
-        // sticky: only raised; in-place reads: a miss does not stop the layer
-        if (!sticky || miss > 0) *early_out = (miss > 0 && !host) ? 1u : 0u;
+        if (!sticky || miss > 0) *early_out = miss > 0 ? 1u : 0u;   // sticky: only raised
       }
     } else {
       const int slot = lane < k ? slot_of(sel_res[lane], n_slots) : 0;
-      if (lane < k) {
-        s_slot[lane] = slot;
-        s_id[lane] = sel_ids[lane];
-      }
+      if (lane < k) s_slot[lane] = slot;
       const int miss = __popcll(__ballot(slot < 0));
-      if (lane == 0) s_miss = host ? 0 : miss;
+      if (lane == 0) s_miss = miss;
     }
   } else if (!publisher) {
     const int run = tid - 64;            // H/16 <= 128 runs over waves 1-2
@@ -180,8 +174,8 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
   const int r = blockIdx.x / bpr;
   const int j0 = (blockIdx.x % bpr) * jpb + wv * RPT;
   const int slot = s_slot[r];
-  const uint8_t* tg = expert_tensor(pv, host, slot, s_id[r], 0);
-  const uint8_t* tu = expert_tensor(pv, host, slot, s_id[r], 1);
+  const uint8_t* tg = tensor_base(pv, slot, 0);
+  const uint8_t* tu = tensor_base(pv, slot, 1);
   const int rho = lane & 15, q = lane >> 4;
   const int64_t blk = int64_t(j0 + rho / BPT) * KB + rho % BPT;
   TileCodes cg[NH], cu[NH];
@@ -231,9 +225,8 @@ __host__ __device__ constexpr int decode_down_hf_offset(int nw, int KBD, int k) 
 template <int KBD, int QBITS>
 __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
     PoolView pv, int H, int F, int k, const int32_t* __restrict__ slots,
-    const int32_t* __restrict__ ids, const float* __restrict__ weights,
-    const float* __restrict__ hbuf, const uint32_t* __restrict__ early_out, float* __restrict__ y,
-    const uint8_t* __restrict__ host) {
+    const float* __restrict__ weights, const float* __restrict__ hbuf,
+    const uint32_t* __restrict__ early_out, float* __restrict__ y) {
   constexpr int BPT = KBD < 4 ? KBD : 4;
   constexpr int RPT = 16 / BPT;
   constexpr int NH = KBD / BPT;
@@ -253,13 +246,11 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
   constexpr int NU = (16 * KBD + 63) / 64;   // runs of 16 values per lane
   const uint32_t flag = *early_out;
   __shared__ int s_sl[16][64];           // each wave's copy of the k slots (k <= 32)
-  __shared__ int s_ex[16][64];           // and of the k expert ids (in-place reads only)
   {
     const uint8_t* g = reinterpret_cast<const uint8_t*>(hbuf + int64_t(wv < k ? wv : 0) * F) + 16 * lane;
 #pragma unroll
     for (int c = 0; c < KBD; ++c) __builtin_amdgcn_global_load_lds(g + c * 1024, s_hf + c * 1024, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(slots + (lane < k ? lane : 0), &s_sl[wv][0], 4, 0, 0);
-    if (host) __builtin_amdgcn_global_load_lds(ids + (lane < k ? lane : 0), &s_ex[wv][0], 4, 0, 0);
   }
   if (flag) return;
   const int i0 = blockIdx.x * RPT;
@@ -279,7 +270,7 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
       for (int u = 0; u < NU; ++u) load_run(hr, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
     }
     const int slot = s_sl[wv][r];
-    const uint8_t* td = expert_tensor(pv, host, slot, slot >= 0 ? 0 : s_ex[wv][r], 2);
+    const uint8_t* td = tensor_base(pv, slot, 2);
     TileCodes cd[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) cd[h] = load_tile<QBITS>(td, pv, blk + BPT * h, q);
@@ -321,7 +312,7 @@ static void gateup_mfma(const DecodeArgs& a, hipStream_t st) {
   const int blocks = a.k * (a.F / (4 * (16 / BPT))) + 1;
   decode_topk_gateup_mfma_kernel<N, KB, QBITS><<<blocks, 256, 0, st>>>(
       a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
-      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf, int(a.sticky), a.host);
+      a.weights, a.slots, a.miss_count, a.early_out, a.hbuf, int(a.sticky));
 }
 
 template <int N, int QBITS>
@@ -365,7 +356,7 @@ static void down_mfma(const DecodeArgs& a, hipStream_t st) {
   const int nw = decode_down_mfma_waves(a.k, a.F);
   const size_t lds = size_t(decode_down_hf_offset(nw, KBD, a.k)) + size_t(nw) * KBD * 1024;
   decode_down_sum_mfma_kernel<KBD, QBITS><<<a.H / RPT, 64 * nw, lds, st>>>(
-      a.pool, a.H, a.F, a.k, a.slots, a.ids, a.weights, a.hbuf, a.early_out, a.y, a.host);
+      a.pool, a.H, a.F, a.k, a.slots, a.weights, a.hbuf, a.early_out, a.y);
 }
 
 void launch_decode_down_sum_mfma(const DecodeArgs& a, hipStream_t st) {

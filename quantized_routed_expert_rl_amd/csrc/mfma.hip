@@ -190,8 +190,7 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
     const int32_t* __restrict__ n_items_p, const int32_t* __restrict__ item_bucket,
     const int32_t* __restrict__ item_start, const int32_t* __restrict__ bucket_start,
     const int32_t* __restrict__ bucket_slot, const int32_t* __restrict__ pairs,
-    float* __restrict__ out, const int32_t* __restrict__ bucket_expert, int n_slots,
-    const uint8_t* __restrict__ host) {
+    float* __restrict__ out) {
   if (*early_out) return;
   // the pass's digit operands for every K-block: token t's block kb at
   // t * tstride + kb * 1024, tstride = KB*1024 + 144 (= 9 mod 16 in 16-byte
@@ -228,14 +227,8 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
   // every ring slot is refilled at every step (no data-dependent refills,
   // which would make the compiler copy the ring and wait for it).
   int s_item = r0 / RPI, s_tile = (r0 - s_item * RPI) * 8 + w, s_kb = 0, s_left = NQ;
-  // the item's tensor: its bucket's pool slot, or (in-place reads) the
-  // expert's row of the host store when the slot is not resident
-  auto item_tensor = [&](int it) {
-    const int bb = item_bucket[it];
-    const int sl = bucket_slot[bb];
-    const bool res = unsigned(sl) < unsigned(n_slots) || !host;
-    return expert_tensor(pv, host, res ? sl : -1, res ? 0 : bucket_expert[bb], which);
-  };
+  // the item's tensor in its bucket's pool slot
+  auto item_tensor = [&](int it) { return tensor_base(pv, bucket_slot[item_bucket[it]], which); };
   const uint8_t* s_t = item_tensor(s_item);
   auto next_codes = [&]() {
     const RowCodes rc =
@@ -442,7 +435,7 @@ void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
   auto kern = a.qbits == 3 ? prefill_expert_kernel<true, 3> : prefill_expert_kernel<true, 2>;
   kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
                                    p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
-                                   p.pairs, a.hbuf, p.bucket_expert, a.n_slots, a.host);
+                                   p.pairs, a.hbuf);
 }
 
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
@@ -450,7 +443,7 @@ void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   auto kern = a.qbits == 3 ? prefill_expert_kernel<false, 3> : prefill_expert_kernel<false, 2>;
   kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
                                    p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
-                                   p.pairs, a.ebuf, p.bucket_expert, a.n_slots, a.host);
+                                   p.pairs, a.ebuf);
 }
 
 }  // namespace rl

@@ -61,15 +61,6 @@ __device__ inline const uint8_t* tensor_base(const PoolView& p, int slot, int wh
   return p.base + int64_t(slot) * p.slot_bytes + int64_t(which) * p.tensor_bytes;
 }
 
-// Tensor `which` of a selected expert: its pool slot, or, for a
-// non-resident expert read in place, its row `expert` of the host store
-// (rows of slot_bytes from `host`).
-__device__ inline const uint8_t* expert_tensor(const PoolView& p, const uint8_t* host, int slot,
-                                               int expert, int which) {
-  return slot >= 0 ? tensor_base(p, slot, which)
-                   : host + int64_t(expert) * p.slot_bytes + int64_t(which) * p.tensor_bytes;
-}
-
 // One 32-value group of a tensor, ready for a dot product with 32
 // activations: codes (low bits, 64 bits), third bit plane (3-bit only),
 // group scale factor (2s+1)/16 * d.

@@ -21,7 +21,6 @@ struct RouteArgs {
   int32_t* slots;
   uint32_t* miss_count;
   uint32_t* early_out;
-  bool flag_misses = true;   // false: misses are counted but raise no flag (in-place reads)
 };
 void launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -43,10 +42,6 @@ struct DecodeArgs {
   float* y;
   bool mfma;            // int8 matrix-core expert kernels (F % 256 == 0)
   bool sticky;          // early_out shared and only raised: a set flag stops the call
-  // in-place reads: non-resident experts of this layer are read from host
-  // memory at host + expert * slot_bytes (device-visible address), and the
-  // flag stays clear; NULL = early-out on a miss
-  const uint8_t* host = nullptr;
   // the step before the layer, folded into the router kernel (a_out NULL:
   // none, x is the layer input): r = x_prev + y_prev (x_prev alone when
   // y_prev is NULL or *flag_prev is set), written to x_out when not NULL;
@@ -102,9 +97,6 @@ struct PrefillArgs {
   int32_t* he;      // [T*k][F/256] exponents of h
   float* y;
   int n_slots = 0;
-  // in-place reads: non-resident experts of this layer are read from host
-  // memory at host + expert * slot_bytes (device-visible address); NULL = none
-  const uint8_t* host = nullptr;
 };
 void launch_prefill_plan(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_gateup(const PrefillArgs& a, hipStream_t st);

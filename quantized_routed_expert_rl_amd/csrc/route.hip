@@ -159,7 +159,7 @@ template <int N>
 __global__ __launch_bounds__(64) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int layer, int n_slots,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
-    uint32_t* miss_count, uint32_t* early_out, int flag_misses) {
+    uint32_t* miss_count, uint32_t* early_out) {
   __shared__ __align__(16) TopkLds s_tk;
   __shared__ int sel_ids[32];
   __shared__ float sel_lg[32];
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
                                 weights + int64_t(t) * k, slots + int64_t(t) * k);
   if ((threadIdx.x & 63) == 0 && miss > 0) {
     atomicAdd(miss_count, uint32_t(miss));
-    if (flag_misses) atomicOr(early_out, 1u);
+    atomicOr(early_out, 1u);
   }
 }
 
@@ -180,7 +180,7 @@ template <int N>
 static void launch_topk_n(const RouteArgs& a, hipStream_t st) {
   route_topk_kernel<N><<<a.T, 64, 0, st>>>(a.logits, a.T, a.E, a.k, a.layer, a.n_slots,
                                            a.residency, a.ids, a.weights, a.slots,
-                                           a.miss_count, a.early_out, a.flag_misses ? 1 : 0);
+                                           a.miss_count, a.early_out);
 }
 
 int cand_per_lane(int E) {

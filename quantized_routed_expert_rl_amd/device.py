@@ -91,13 +91,7 @@ class DeviceModel:
         return B.rl_route(self.desc, layer, x.shape[0], x, self.router[layer], self.bias[layer],
                           self.residency, out.c(), scratch, scratch.numel(), stream)
 
-    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None, desc=None,
-               host_store=None):
-        if host_store is not None:            # missing experts read in place
-            return B.moe_decode_layer_mapped(desc or self.desc, layer, x, self.router[layer],
-                                             self.bias[layer], self.residency, self.pool,
-                                             host_store, out.c(), scratch, scratch.numel(), y,
-                                             stream)
+    def decode(self, layer, x, out: RouteBuffers, scratch, y, stream=None, desc=None):
         return B.moe_decode_layer(desc or self.desc, layer, x, self.router[layer], self.bias[layer],
                                   self.residency, self.pool, out.c(), scratch, scratch.numel(),
                                   y, stream)
@@ -111,13 +105,7 @@ class DeviceModel:
                                         self.residency, self.pool, out.c(), scratch,
                                         scratch.numel(), y, stream)
 
-    def prefill(self, layer, x, plan_cap, out: RouteBuffers, scratch, y, stream=None,
-                host_store=None):
-        if host_store is not None:            # missing experts read in place
-            return B.moe_prefill_chunk_mapped(self.desc, layer, x.shape[0], plan_cap, x,
-                                              self.router[layer], self.bias[layer],
-                                              self.residency, self.pool, host_store, out.c(),
-                                              scratch, scratch.numel(), y, stream)
+    def prefill(self, layer, x, plan_cap, out: RouteBuffers, scratch, y, stream=None):
         return B.moe_prefill_chunk(self.desc, layer, x.shape[0], plan_cap, x,
                                    self.router[layer], self.bias[layer], self.residency,
                                    self.pool, out.c(), scratch, scratch.numel(), y, stream)

@@ -36,12 +36,9 @@ class DecodeStack:
     its normalised input, ``routes[l]`` its routing results and ``y[l]`` its
     MoE output (left untouched when the layer's flag is set)."""
 
-    def __init__(self, model: DeviceModel, host_store=None):
+    def __init__(self, model: DeviceModel):
         w = model.w
         self.model = model
-        # a pinned store of every expert: missing experts are read from it in
-        # place (moe_decode_layer_mapped) and no layer stops
-        self.host_store = host_store
         self.L, self.H = w.n_layers, w.hidden
         self.x = torch.empty(self.L + 1, self.H, device=DEV)
         self.a = torch.empty(self.L + 1, self.H, device=DEV)   # a[L]: norm of the output
@@ -52,29 +49,21 @@ class DecodeStack:
 
     def token(self, x0: torch.Tensor) -> torch.Tensor:
         """Runs x0 [H] (device) through the stack on the current stream.
-        Without a host store each layer's call also does the step before it
-        (the previous layer's residual add and this layer's RMSNorm) in its
-        first kernel (moe_decode_layer_after), one launch less per layer, with
-        the same bits as the separate launch."""
+        Each layer's call also does the step before it (the previous layer's
+        residual add and this layer's RMSNorm) in its first kernel
+        (moe_decode_layer_after), one launch less per layer, with the same
+        bits as the separate launch."""
         self.x[0].copy_(x0.reshape(self.H))
-        if self.host_store is None:
-            for l in range(self.L):
-                first = l == 0
-                self.model.decode_after(
-                    l, self.x[0] if first else self.x[l - 1], None if first else self.y[l - 1],
-                    None if first else self.routes[l - 1].early_out, EPS,
-                    None if first else self.x[l], self.a[l], self.routes[l], self.scratch,
-                    self.y[l])
-            l = self.L - 1
-            B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
-                                  self.x[l + 1], self.a[l + 1], EPS)
-            return self.x[self.L]
-        B.rl_rmsnorm(1, self.H, self.x[0], self.a[0], EPS)
         for l in range(self.L):
-            self.model.decode(l, self.a[l], self.routes[l], self.scratch, self.y[l],
-                              host_store=self.host_store)
-            B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
-                                  self.x[l + 1], self.a[l + 1], EPS)
+            first = l == 0
+            self.model.decode_after(
+                l, self.x[0] if first else self.x[l - 1], None if first else self.y[l - 1],
+                None if first else self.routes[l - 1].early_out, EPS,
+                None if first else self.x[l], self.a[l], self.routes[l], self.scratch,
+                self.y[l])
+        l = self.L - 1
+        B.rl_residual_rmsnorm(1, self.H, self.x[l], self.y[l], self.routes[l].early_out,
+                              self.x[l + 1], self.a[l + 1], EPS)
         return self.x[self.L]
 
 
@@ -84,11 +73,9 @@ class PrefillStack:
     layer's input [n_c x H], ``as_[c][l]`` the normalised input,
     ``routes[c][l]`` the routing results and ``ys[c][l]`` the MoE output."""
 
-    def __init__(self, model: DeviceModel, chunks: Sequence[int], plan_cap: int,
-                 host_store=None):
+    def __init__(self, model: DeviceModel, chunks: Sequence[int], plan_cap: int):
         w = model.w
         self.model = model
-        self.host_store = host_store          # missing experts read in place from it
         self.L, self.H = w.n_layers, w.hidden
         self.chunks = list(chunks)
         self.plan_cap = plan_cap
@@ -110,7 +97,7 @@ class PrefillStack:
             B.rl_rmsnorm(n, self.H, x[0], self.as_[c][0], EPS)
             for l in range(self.L):
                 self.model.prefill(l, self.as_[c][l], self.plan_cap, self.routes[c][l],
-                                   self.scratch, self.ys[c][l], host_store=self.host_store)
+                                   self.scratch, self.ys[c][l])
                 B.rl_residual_rmsnorm(n, self.H, x[l], self.ys[c][l], self.routes[c][l].early_out,
                                       x[l + 1], self.as_[c][l + 1], EPS)
             outs.append(x[self.L])

@@ -53,12 +53,6 @@ WORKLOADS = {
     # 48 stacked prefill layers over a 1100-token prompt, Zipf routing.
     "prefill_48l": Workload("prefill_48l", 4, 2048, 512, 10, 512, 48, 1100,
                             chunks=(512, 512, 76), plan_cap=512, zipf=True),
-    # The same prompt through the bounded pool of decode_48l_hot (same
-    # stream id: same experts, router and resident set), misses read in
-    # place from host memory.
-    "prefill_48l_hot": Workload("prefill_48l_hot", 5, 2048, 512, 10, 512, 48, 1100,
-                                chunks=(512, 512, 76), plan_cap=512, zipf=True,
-                                resident=48 * 224, popular=True),
 }
 
 

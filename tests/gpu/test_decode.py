@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu.common import check_route, close, oracle_route, shape_of
+from gpu.common import HostInputs, check_route, close, oracle_decode_many, oracle_route, shape_of
 from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import synth, workloads
 from quantized_routed_expert_rl_amd.device import DeviceModel, RouteBuffers, to_dev
@@ -52,8 +52,7 @@ def test_route_tiny_gemv_and_gemm(tiny):
         out = RouteBuffers.alloc(T, w.top_k, w.n_experts)
         scratch = torch.zeros(64 << 10, dtype=torch.uint8, device="cuda")
         tiny.route(0, to_dev(x[:T]), out, scratch)
-        sub = O.route(x[:T], tiny.router[0].cpu().numpy(), None, tiny.table[0], w.top_k)
-        check_route(out, sub)
+        check_route(out, oracle_route(tiny, 0, x[:T]))
     assert ref.ids.shape == (4, 2)
 
 
@@ -61,45 +60,33 @@ def test_decode_tiny(tiny):
     w = tiny.w
     x = synth.activations(w, 4)
     outs, ys = _decode_tokens(tiny, x)
-    for t in range(4):
-        r, y_ref, _ = O.decode_layer(shape_of(w), x[t], tiny.router[0].cpu().numpy(), None,
-                                     tiny.table[0], tiny.read_slot)
+    host = HostInputs.of(tiny)
+    for t, (r, y_ref, _) in enumerate(oracle_decode_many(host, 0, x, tiny.table[0])):
         check_route(outs[t], r)
         close(ys[t].cpu().numpy(), y_ref, f"y token {t}")
 
 
-def test_decode_real_shape_sampled(real):
-    """Single-token decode at hidden 2048, 512 experts, top-10, width 512: ids and
-    slots of 64 tokens exact; y of 6 of them against the oracle."""
-    w = real.w
-    x = synth.activations(w, 64, stream=7)
-    outs, ys = _decode_tokens(real, x)
-    ref = oracle_route(real, 0, x)
-    for t in range(64):
-        assert np.array_equal(outs[t].ids.cpu().numpy()[0], ref.ids[t]), t
-        assert np.array_equal(outs[t].slots.cpu().numpy()[0], ref.slots[t]), t
-        close(outs[t].weights.cpu().numpy()[0], ref.weights[t], f"weights {t}")
-        close(outs[t].logits.cpu().numpy()[0], ref.logits[t], f"logits {t}")
-    for t in (0, 1, 17, 33, 50, 63):
-        _, y_ref, _ = O.decode_layer(shape_of(w), x[t], real.router[0].cpu().numpy(), None,
-                                     real.table[0], real.read_slot)
-        close(ys[t].cpu().numpy(), y_ref, f"y token {t}")
+def _check_real(model, x, what):
+    """Every token: ids, slots, miss count and flag exact; logits, weights and
+    all H values of y within tolerance of the oracle."""
+    outs, ys = _decode_tokens(model, x)
+    host = HostInputs.of(model)
+    refs = oracle_decode_many(host, 0, x, model.table[0])
+    for t, (r, y_ref, _) in enumerate(refs):
+        check_route(outs[t], r)
+        close(ys[t].cpu().numpy(), y_ref, f"y token {t} ({what})")
 
 
-def test_decode_real_shape_3bit_sampled(real3):
+def test_decode_real_shape(real):
+    """Single-token decode at hidden 2048, 512 experts, top-10, width 512:
+    64 tokens, every output against the oracle."""
+    _check_real(real, synth.activations(real.w, 64, stream=7), "2-bit")
+
+
+def test_decode_real_shape_3bit(real3):
     """The same layer with 3-bit block weights (third code bit in its own
-    plane): ids and slots of 24 tokens exact, y of 4 against the oracle."""
-    w = real3.w
-    x = synth.activations(w, 24, stream=8)
-    outs, ys = _decode_tokens(real3, x)
-    ref = oracle_route(real3, 0, x)
-    for t in range(24):
-        assert np.array_equal(outs[t].ids.cpu().numpy()[0], ref.ids[t]), t
-        assert np.array_equal(outs[t].slots.cpu().numpy()[0], ref.slots[t]), t
-    for t in (0, 5, 13, 23):
-        _, y_ref, _ = O.decode_layer(shape_of(w), x[t], real3.router[0].cpu().numpy(), None,
-                                     real3.table[0], real3.read_slot)
-        close(ys[t].cpu().numpy(), y_ref, f"y token {t} (3-bit)")
+    plane): 32 tokens, every output against the oracle."""
+    _check_real(real3, synth.activations(real3.w, 32, stream=8), "3-bit")
 
 
 def test_decode_early_out_leaves_y(real):

@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 import torch
 
+from gpu.common import RTOL, ATOL, HostInputs, pool_map
+from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import synth
 from quantized_routed_expert_rl_amd.device import DeviceModel, to_dev
 from quantized_routed_expert_rl_amd.stack import (DecodeStack, HostExpertStore,
@@ -17,6 +19,29 @@ from quantized_routed_expert_rl_amd.stack import (DecodeStack, HostExpertStore,
 from quantized_routed_expert_rl_amd.workloads import Workload
 
 pytestmark = pytest.mark.gpu
+
+
+def oracle_replay_layer_inputs(x, host: HostInputs):
+    """The native driver exposes each layer's input x_l; every layer is
+    checked against the oracle from it: the oracle runs layer l on
+    rmsnorm(x_l) with every expert's true bytes, and x_{l+1} must be the
+    float32 sum of x_l and a y within the tolerance of the oracle's:
+    |x_{l+1} - (x_l + y_ref)| <= 1e-5 + 1e-4 |y_ref| + half an ulp of x_{l+1}
+    (the one rounding of the residual sum).  A wrong selection, a wrong
+    expert in a slot or a skipped layer moves x_{l+1} far outside that."""
+    w = host.w
+    shape = O.LayerShape(w.hidden, w.n_experts, w.top_k, w.width, w.qbits)
+    every = np.arange(w.n_experts, dtype=np.int32)
+    refs = pool_map(lambda l: O.decode_layer(shape, O.rmsnorm(x[l])[0], host.router(l),
+                                             host.bias(l), every, lambda e: host.expert(l, e)),
+                    range(w.n_layers))
+    for l, (r, y_ref, _) in enumerate(refs):
+        assert not r.early_out
+        want = x[l].astype(np.float64) + y_ref.astype(np.float64)
+        bound = ATOL + RTOL * np.abs(y_ref.astype(np.float64)) + 0.5 * np.spacing(
+            np.abs(x[l + 1])).astype(np.float64)
+        err = np.abs(x[l + 1].astype(np.float64) - want)
+        assert (err <= bound).all(), f"layer {l}: worst excess {float((err - bound).max()):.3e}"
 
 
 def _workloads(per_layer):
@@ -38,6 +63,7 @@ def test_native_driver_equals_python_stack(per_layer, limit, prefetch, sticky):
                              sticky=sticky)
     nat = NativeServicedDecode(DeviceModel(hot), store, early_out_limit=limit, prefetch=prefetch,
                                sticky=sticky)
+    host = HostInputs(hot)
     for t in range(hot.tokens):
         print("token", t, flush=True)
         x0 = to_dev(xs[t])
@@ -48,6 +74,7 @@ def test_native_driver_equals_python_stack(per_layer, limit, prefetch, sticky):
         want = ref.x.cpu().numpy()
         assert np.array_equal(py.stack.x.cpu().numpy(), want), f"python stack, token {t}"
         assert np.array_equal(nat.x.cpu().numpy(), want), f"native driver, token {t}"
+        oracle_replay_layer_inputs(nat.x.cpu().numpy(), host)
     assert nat.stats == py.stats, (nat.stats, py.stats)
     assert nat.cache.stats() == py.cache.stats()
     assert np.array_equal(nat.model.residency.cpu().numpy(), nat.cache.table())

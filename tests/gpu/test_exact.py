@@ -3,8 +3,7 @@ step of the expert path is exact in float32, so the kernels' y must equal the
 exact value to the last bit (decode and prefill, 2-bit and 3-bit, at
 hidden = width = 256 and at the real shape hidden 2048, width 512), a
 stronger check than the tolerance the other parity tests apply.  Width 128
-takes the vector-unit kernels; the in-place reads of non-resident experts
-from pinned host memory (the _mapped entry points) are checked the same way.
+takes the vector-unit kernels.
 
 The layer follows the definitions of the routed expert (SwiGLU gate/up,
 down, rank-ordered sum; "Red Lite dev20 - batched prompt ingestion" and
@@ -121,46 +120,22 @@ def _same_bits(got, want, what):
                            f"worst |d|={np.abs(got - want)[bad].max():.3e}")
 
 
-def _pinned(a):
-    t = torch.empty(a.shape, dtype=torch.uint8, pin_memory=True)
-    t.numpy()[...] = a
-    return t
-
-
 @pytest.mark.parametrize("H,F,qbits", SHAPES)
 def test_decode_exact(H, F, qbits):
-    _decode_exact(H, F, qbits, mapped=False)
-
-
-@pytest.mark.parametrize("qbits", [2, 3])
-def test_decode_mapped_exact(qbits):
-    _decode_exact(2048, 512, qbits, mapped=True)
-
-
-def _decode_exact(H, F, qbits, mapped):
     pool_np, nums, W, x = _layer(H, F, qbits, 1)
     table = np.arange(E, dtype=np.int32)[None, :]
-    # in-place reads: half of the experts are not resident and come from the store
-    res_table = np.where(table % 2 == 1, -1, table).astype(np.int32) if mapped else table
     d = B.desc(H, E, K, F, 1, qbits, E)
-    pool, Wd, res = to_dev(pool_np), to_dev(W), to_dev(res_table)
-    store = _pinned(pool_np) if mapped else None
+    pool, Wd, res = to_dev(pool_np), to_dev(W), to_dev(table)
     scratch = torch.zeros(B.rl_decode_scratch_bytes(d), dtype=torch.uint8, device="cuda")
     shape = O.LayerShape(H, E, K, F, qbits)
     for t in range(T):
         out = RouteBuffers.alloc(1, K, E)
         y = torch.full((H,), float("nan"), device="cuda")
-        if mapped:
-            B.moe_decode_layer_mapped(d, 0, to_dev(x[t:t + 1]), Wd, None, res, pool, store,
-                                      out.c(), scratch, scratch.numel(), y)
-        else:
-            B.moe_decode_layer(d, 0, to_dev(x[t:t + 1]), Wd, None, res, pool, out.c(), scratch,
-                               scratch.numel(), y)
+        B.moe_decode_layer(d, 0, to_dev(x[t:t + 1]), Wd, None, res, pool, out.c(), scratch,
+                           scratch.numel(), y)
         r, y_ref, _ = O.decode_layer(shape, x[t], W, None, table[0], lambda s: pool_np[s])
         torch.cuda.synchronize()
-        assert np.array_equal(out.ids.cpu().numpy(), r.ids)
-        if not mapped:
-            check_route(out, r)
+        check_route(out, r)
         assert float(out.weights.cpu()[0, 0]) == 1.0
         want = _exact_y(nums, int(r.ids[0][0]), x[t])
         _same_bits(y_ref, want, f"oracle token {t}")
@@ -169,35 +144,19 @@ def _decode_exact(H, F, qbits, mapped):
 
 @pytest.mark.parametrize("H,F,qbits", SHAPES)
 def test_prefill_exact(H, F, qbits):
-    _prefill_exact(H, F, qbits, mapped=False)
-
-
-@pytest.mark.parametrize("qbits", [2, 3])
-def test_prefill_mapped_exact(qbits):
-    _prefill_exact(2048, 512, qbits, mapped=True)
-
-
-def _prefill_exact(H, F, qbits, mapped):
     pool_np, nums, W, x = _layer(H, F, qbits, 2)
     table = np.arange(E, dtype=np.int32)[None, :]
-    res_table = np.where(table % 2 == 1, -1, table).astype(np.int32) if mapped else table
     d = B.desc(H, E, K, F, 1, qbits, E)
     pool = to_dev(pool_np)
     scratch = torch.zeros(B.rl_prefill_scratch_bytes(d, T), dtype=torch.uint8, device="cuda")
     out = RouteBuffers.alloc(T, K, E)
     y = torch.full((T, H), float("nan"), device="cuda")
-    if mapped:
-        B.moe_prefill_chunk_mapped(d, 0, T, E, to_dev(x), to_dev(W), None, to_dev(res_table),
-                                   pool, _pinned(pool_np), out.c(), scratch, scratch.numel(), y)
-    else:
-        B.moe_prefill_chunk(d, 0, T, E, to_dev(x), to_dev(W), None, to_dev(res_table), pool,
-                            out.c(), scratch, scratch.numel(), y)
+    B.moe_prefill_chunk(d, 0, T, E, to_dev(x), to_dev(W), None, to_dev(table), pool, out.c(),
+                        scratch, scratch.numel(), y)
     r, _, y_ref = O.prefill_chunk(O.LayerShape(H, E, K, F, qbits), x, W, None, table[0],
                                   lambda s: pool_np[s], E)
     torch.cuda.synchronize()
-    assert np.array_equal(out.ids.cpu().numpy(), r.ids)
-    if not mapped:
-        check_route(out, r)
+    check_route(out, r)
     got = y.cpu().numpy()
     for t in range(T):
         want = _exact_y(nums, int(r.ids[t][0]), x[t])

@@ -21,7 +21,7 @@ def _rows(T, H, seed):
     return (rng.standard_normal((T, H)) * rng.uniform(0.1, 10.0, (T, 1))).astype(np.float32)
 
 
-@pytest.mark.parametrize("T,H", [(1, 256), (5, 2048), (3, 768)])
+@pytest.mark.parametrize("T,H", [(1, 256), (5, 2048), (3, 768), (2, 1280), (3, 1536)])
 def test_rmsnorm(T, H):
     x = _rows(T, H, T * H)
     out = torch.full((T, H), float("nan"), device="cuda")
@@ -41,8 +41,10 @@ def test_residual_add(flag):
 
 
 @pytest.mark.parametrize("flag", [None, 0, 1])
-@pytest.mark.parametrize("T,H", [(1, 2048), (7, 512)])
+@pytest.mark.parametrize("T,H", [(1, 2048), (7, 512), (2, 1280), (3, 1536), (1, 768)])
 def test_residual_rmsnorm(flag, T, H):
+    """Hidden sizes whose last 1024-value stride is partly used (1280, 1536,
+    768) take the norms' ragged chunk loop."""
     x, y = _rows(T, H, 3 + T), _rows(T, H, 4 + H)
     fl = None if flag is None else torch.tensor([flag], dtype=torch.int32, device="cuda")
     xo = torch.full((T, H), float("nan"), device="cuda")

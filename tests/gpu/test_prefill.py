@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu.common import check_route, close, oracle_route, shape_of
+from gpu.common import HostInputs, check_route, close, oracle_prefill, oracle_route, shape_of
 from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import binding as B
 from quantized_routed_expert_rl_amd import synth, workloads
@@ -51,8 +51,7 @@ def test_prefill_tiny(tiny, plan_cap):
     w = tiny.w
     x = synth.activations(w, w.tokens)
     out, y, scratch = run_chunk(tiny, x, plan_cap)
-    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, tiny.router[0].cpu().numpy(), None,
-                                     tiny.table[0], tiny.read_slot, plan_cap)
+    r, plan, y_ref = oracle_prefill(HostInputs.of(tiny), 0, x, tiny.table[0], plan_cap)
     check_route(out, r)
     check_plan(tiny, scratch, w.tokens, plan, w.tokens, w.top_k)
     close(y.cpu().numpy(), y_ref, "y")
@@ -63,44 +62,31 @@ def test_prefill_tiny_ragged(tiny, T, plan_cap):
     w = tiny.w
     x = synth.activations(w, T, stream=T)
     out, y, scratch = run_chunk(tiny, x, plan_cap, max_tokens=T + 5)
-    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, tiny.router[0].cpu().numpy(), None,
-                                     tiny.table[0], tiny.read_slot, plan_cap)
+    r, plan, y_ref = oracle_prefill(HostInputs.of(tiny), 0, x, tiny.table[0], plan_cap)
     check_route(out, r)
     check_plan(tiny, scratch, T, plan, T, w.top_k)      # plan layout of a T-token call
     close(y.cpu().numpy(), y_ref, "y")
 
 
-def test_prefill_real_chunk_sampled(real):
-    """A 512-token chunk at real shape: every id, slot and the whole plan exact;
-    y of 12 sampled tokens against the oracle."""
-    w = real.w
-    x = synth.activations(w, 512)
-    out, y, scratch = run_chunk(real, x, 512)
-    sample = [0, 1, 2, 100, 255, 256, 300, 411, 500, 509, 510, 511]
-    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, real.router[0].cpu().numpy(), None,
-                                     real.table[0], real.read_slot, 512, tokens=sample)
+def _check_real_chunk(model, x, what):
+    """A 512-token chunk at real shape (5120 pairs over the 512 experts):
+    every id, slot and the whole plan exact; all 512 x 2048 values of y
+    against the oracle."""
+    w = model.w
+    out, y, scratch = run_chunk(model, x, 512)
+    r, plan, y_ref = oracle_prefill(HostInputs.of(model), 0, x, model.table[0], 512)
     check_route(out, r)
-    check_plan(real, scratch, 512, plan, 512, w.top_k)
-    yg = y.cpu().numpy()
-    close(yg[sample], y_ref[sample], "y sample")
-    assert not np.isnan(yg).any()
+    check_plan(model, scratch, 512, plan, 512, w.top_k)
+    close(y.cpu().numpy(), y_ref, f"y ({what})")
 
 
-def test_prefill_real_chunk_3bit_sampled():
-    """A 512-token chunk with 3-bit block weights: routing and plan exact, y of
-    6 sampled tokens against the oracle."""
+def test_prefill_real_chunk(real):
+    _check_real_chunk(real, synth.activations(real.w, 512), "2-bit")
+
+
+def test_prefill_real_chunk_3bit():
     m3 = DeviceModel(workloads.get("prefill_1l", 3))
-    w = m3.w
-    x = synth.activations(w, 512, stream=5)
-    out, y, scratch = run_chunk(m3, x, 512)
-    sample = [0, 3, 200, 256, 480, 511]
-    r, plan, y_ref = O.prefill_chunk(shape_of(w), x, m3.router[0].cpu().numpy(), None,
-                                     m3.table[0], m3.read_slot, 512, tokens=sample)
-    check_route(out, r)
-    check_plan(m3, scratch, 512, plan, 512, w.top_k)
-    yg = y.cpu().numpy()
-    close(yg[sample], y_ref[sample], "y sample (3-bit)")
-    assert not np.isnan(yg).any()
+    _check_real_chunk(m3, synth.activations(m3.w, 512, stream=5), "3-bit")
 
 
 def test_prefill_plan_cap_and_chunk_invariance(real):

@@ -16,6 +16,8 @@ import numpy as np
 import pytest
 import torch
 
+from gpu.common import HostInputs, close, pool_map
+from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import synth
 from quantized_routed_expert_rl_amd.device import DeviceModel, to_dev
 from quantized_routed_expert_rl_amd.stack import DecodeStack, HostExpertStore, ServicedDecodeStack
@@ -29,6 +31,36 @@ def _workloads(per_layer):
                    popular=True)
     full = Workload(**{**hot.__dict__, "resident": -1, "popular": False})
     return hot, full
+
+
+def oracle_replay_serviced(svc: ServicedDecodeStack, host: HostInputs):
+    """Every layer of the token just run, against the oracle in replay mode:
+    the oracle takes the GPU's a_l and every expert's true bytes (regenerated
+    on the host), so its selection must equal the GPU's, its y must match
+    within tolerance, and x_{l+1} must be the exact float32 sum x_l + y_l.
+    After service every layer ran with its whole selection resident: no
+    flag, no miss, and each selected expert's slot in the device pool holds
+    that expert's bytes (the copy the cache planned went where it said)."""
+    s = svc.stack
+    w = host.w
+    torch.cuda.synchronize()
+    x, a, y = s.x.cpu().numpy(), s.a.cpu().numpy(), s.y.cpu().numpy()
+    shape = O.LayerShape(w.hidden, w.n_experts, w.top_k, w.width, w.qbits)
+    every = np.arange(w.n_experts, dtype=np.int32)        # all resident: slot = expert id
+    refs = pool_map(lambda l: O.decode_layer(shape, a[l], host.router(l), host.bias(l), every,
+                                             lambda e: host.expert(l, e)), range(w.n_layers))
+    for l, (r, y_ref, _) in enumerate(refs):
+        close(a[l], O.rmsnorm(x[l])[0], f"rmsnorm layer {l}")
+        ids = s.routes[l].ids.cpu().numpy()[0]
+        slots = s.routes[l].slots.cpu().numpy()[0]
+        assert np.array_equal(ids, r.ids[0]), f"ids layer {l}"
+        close(s.routes[l].weights.cpu().numpy()[0], r.weights[0], f"weights layer {l}")
+        assert (slots >= 0).all(), f"layer {l} still misses"
+        for e, sl in zip(ids, slots):
+            assert np.array_equal(svc.model.pool[int(sl)].cpu().numpy(), host.expert(l, int(e))), \
+                f"slot {sl} of layer {l} does not hold expert {e}"
+        close(y[l], y_ref, f"y layer {l}")
+        assert np.array_equal(x[l + 1], O.residual_add(x[l], y[l])), f"residual layer {l}"
 
 
 @pytest.mark.parametrize("per_layer,limit,prefetch,sticky", [
@@ -45,9 +77,10 @@ def test_serviced_stack_equals_resident_stack(per_layer, limit, prefetch, sticky
         want.append(ref.x.cpu().numpy().copy())
     svc = ServicedDecodeStack(DeviceModel(hot), HostExpertStore(hot), early_out_limit=limit,
                               prefetch=prefetch, sticky=sticky)
+    host = HostInputs(hot)
     for t in range(hot.tokens):
         svc.token(to_dev(xs[t]))
-        torch.cuda.synchronize()
+        oracle_replay_serviced(svc, host)
         got = svc.stack.x.cpu().numpy()
         for l in range(hot.n_layers + 1):
             assert np.array_equal(got[l], want[t][l]), f"token {t} layer {l}"

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu.common import close, shape_of
+from gpu.common import HostInputs, close, oracle_decode_many
 from oracle import moe_oracle as O
 from quantized_routed_expert_rl_amd import binding as B
 from quantized_routed_expert_rl_amd import synth
@@ -73,9 +73,7 @@ def test_clear_flag_stays_clear_without_misses(F):
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     _call(m, 1, x, out, flag, y)
     assert int(flag.cpu()[0]) == 0 and int(out.miss_count.cpu()[0]) == 0
-    reader = lambda s: m.read_slot(s)
-    r, y_ref, _ = O.decode_layer(shape_of(m.w), x, m.router[1].cpu().numpy(), None, m.table[1],
-                                 reader)
+    r, y_ref, _ = oracle_decode_many(HostInputs.of(m), 1, x[None], m.table[1])[0]
     assert np.array_equal(out.ids.cpu().numpy()[0], r.ids[0])
     close(y.cpu().numpy(), y_ref, "y")
 
@@ -85,7 +83,8 @@ def test_chain_stops_at_the_first_miss(F):
     m0 = _model(F)
     x = synth.activations(m0.w, 1)[0]
     # layer 1 loses the expert it selects first; layers 0 and 2 keep theirs
-    r1 = O.route(x[None], m0.router[1].cpu().numpy(), None, m0.table[1], m0.w.top_k)
+    host = HostInputs.of(m0)
+    r1 = O.route(x[None], host.router(1), host.bias(1), m0.table[1], m0.w.top_k)
     table = m0.table.copy()
     table[1, r1.ids[0][0]] = -1
     m = _model(F, table=table)

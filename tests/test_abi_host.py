@@ -114,16 +114,26 @@ def test_decode_after_argument_checks():
     d = B.desc(2048, 512, 10, 512, 2, 2, 512)
     out = B.route_out(0x100, 0x100, 0x100, 0x100, 0x100)
     sb = B.rl_decode_scratch_bytes(d)
+    V = 2048 * 4                                                # bytes of one hidden vector
+    XP, YP, XO, AO = 0x10000, 0x20000, 0x30000, 0x40000       # disjoint vectors
 
-    def call(x_prev=0x1000, y_prev=0x2000, flag=0x100, eps=1e-6, x_out=0x3000, a_out=0x4000,
-             pool=0x1000, nbytes=sb):
+    def call(x_prev=XP, y_prev=YP, flag=0x100, eps=1e-6, x_out=XO, a_out=AO, pool=0x1000,
+             nbytes=sb):
         return B.lib.moe_decode_layer_after(C.byref(d), 0, x_prev, y_prev, flag, eps, x_out, a_out,
                                             0x1000, None, 0x1000, pool, C.byref(out), 0x1000,
                                             nbytes, 0x5000, None)
     assert call(a_out=None) == B.RL_E_INVAL                     # a_out is required
-    assert call(x_out=0x1000) == B.RL_E_INVAL                   # r over x_prev
-    assert call(a_out=0x2000) == B.RL_E_INVAL                   # a over y_prev
-    assert call(x_out=0x4000) == B.RL_E_INVAL                   # r over a
+    assert call(x_out=XP) == B.RL_E_INVAL                       # r over x_prev
+    assert call(a_out=YP) == B.RL_E_INVAL                       # a over y_prev
+    assert call(x_out=AO) == B.RL_E_INVAL                       # r over a
+    # partial overlaps: an output that starts inside, or ends inside, an input
+    assert call(x_out=XP + 16) == B.RL_E_INVAL
+    assert call(x_out=XP - V + 16) == B.RL_E_INVAL
+    assert call(a_out=YP + V - 16) == B.RL_E_INVAL
+    assert call(a_out=YP - V + 16) == B.RL_E_INVAL
+    assert call(a_out=XO + 16) == B.RL_E_INVAL                  # a over the tail of r
+    assert call(x_out=AO + V - 16) == B.RL_E_INVAL
+    assert call(y_prev=None, a_out=XP + 4096) == B.RL_E_INVAL   # over x_prev with no y_prev
     assert call(x_out=0x3004) == B.RL_E_INVAL                   # misaligned
     assert call(y_prev=0x2008) == B.RL_E_INVAL
     assert call(pool=None) == B.RL_E_INVAL

@@ -376,3 +376,30 @@ def test_rmsnorm_closed_form():
 def test_residual_skip_is_identity():
     x = np.random.default_rng(11).standard_normal(32).astype(np.float32)
     assert np.array_equal(O.residual_add(x, None), x)
+
+
+def test_residual_add_is_one_correctly_rounded_sum():
+    """The add branch: x + y rounded once to the nearest float32, ties to
+    even (IEEE 754 binary32 values, written out as exact integers and powers
+    of two).  A sequence of f32 operations, a truncating conversion or a
+    round-half-up would each fail one of these."""
+    p24 = 2.0 ** 24
+    cases = [
+        (1.5, 0.25, 1.75),                            # exact sum
+        (p24, 1.0, p24),                              # tie at ulp 2: even neighbour below
+        (p24 + 2.0, 1.0, p24 + 4.0),                  # tie at ulp 2: even neighbour above
+        (p24, 1.5, p24 + 2.0),                        # above the tie: rounds up
+        (1.0, 2.0 ** -24, 1.0),                       # tie at ulp 2^-23: even neighbour 1.0
+        (1.0, 3.0 * 2.0 ** -25, 1.0 + 2.0 ** -23),    # above the tie
+        (-p24, -1.0, -p24),                           # negative tie
+        (3.0, -3.0, 0.0),                             # cancellation
+    ]
+    x = np.array([c[0] for c in cases], np.float32)
+    y = np.array([c[1] for c in cases], np.float32)
+    want = np.array([c[2] for c in cases], np.float32)
+    got = O.residual_add(x, y)
+    assert got.dtype == np.float32
+    assert np.array_equal(got, want), (got, want)
+    # the sum is applied element by element to whole rows
+    xr = np.tile(x, (3, 1))
+    assert np.array_equal(O.residual_add(xr, np.tile(y, (3, 1))), np.tile(want, (3, 1)))
