@@ -203,6 +203,27 @@ int moe_decode_layer_after(const rl_moe_desc* d, int32_t layer, const float* x_p
                            const void* slot_pool, const rl_route_out* route, void* scratch,
                            int64_t scratch_bytes, float* y, void* stream);
 
+/* moe_decode_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call and results without the scratch arguments.  The
+ * scratch lives in a fixed device array of RL_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU, held until the process ends; the call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Layers whose rl_decode_scratch_bytes exceeds that size return
+ * RL_E_SCRATCH with nothing enqueued (the hidden-2048, 512-expert, top-10,
+ * width-512 layer needs 22,528 bytes).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap in time on one GPU -- on different
+ * streams, or from several host threads -- race and give undefined results;
+ * serialise them (one stream, or events).  The first call on a device looks
+ * up the array's address on it (RL_E_DEVICE if that fails); the other errors
+ * are those of moe_decode_layer and come before any device call. */
+#define RL_NOALLOC_SCRATCH_BYTES 65536
+int moe_decode_layer_noalloc(const rl_moe_desc* d, int32_t layer, const float* x,
+                             const float* router_w, const float* router_bias,
+                             const int32_t* residency, const void* slot_pool,
+                             const rl_route_out* route, float* y, void* stream);
+
 /* One prefill chunk of n_tokens tokens through layer `layer` (dev20 "What
  * changed"): route every token, build the chunk's plan -- consecutive token
  * groups whose union of selected experts stays within plan_cap (a token

@@ -63,6 +63,9 @@ _SIGS = {
                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.POINTER(RlRouteOut), C.c_void_p, C.c_int64,
                                          C.c_void_p, C.c_void_p]),
+    "moe_decode_layer_noalloc": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.POINTER(RlRouteOut), C.c_void_p, C.c_void_p]),
     "moe_prefill_chunk": (C.c_int, [C.POINTER(RlMoeDesc), C.c_int32, C.c_int32, C.c_int32,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.POINTER(RlRouteOut), C.c_void_p, C.c_int64, C.c_void_p,
@@ -208,6 +211,17 @@ def moe_decode_layer_after(d, layer, x_prev, y_prev, flag_prev, eps, x_out, a_ou
                                             _ptr(slot_pool), C.byref(route), _ptr(scratch),
                                             scratch_bytes, _ptr(y), _stream(stream)),
                  "moe_decode_layer_after")
+
+
+def moe_decode_layer_noalloc(d, layer, x, router_w, router_bias, residency, slot_pool,
+                             route: RlRouteOut, y, stream=None) -> int:
+    return check(lib.moe_decode_layer_noalloc(C.byref(d), layer, _ptr(x), _ptr(router_w),
+                                              _ptr(router_bias), _ptr(residency),
+                                              _ptr(slot_pool), C.byref(route), _ptr(y),
+                                              _stream(stream)), "moe_decode_layer_noalloc")
+
+
+RL_NOALLOC_SCRATCH_BYTES = 65536
 
 
 def moe_prefill_chunk(d, layer, n_tokens, plan_cap, x, router_w, router_bias, residency,

@@ -216,6 +216,16 @@ PrefillArgs prefill_args(const rl_moe_desc* d, int32_t layer, int32_t n_tokens, 
 
 }  // namespace
 
+// The argument checks of moe_decode_layer (everything but the scratch size).
+int rl::decode_layer_check(const rl_moe_desc* d, int32_t layer, const float* x,
+                           const float* router_w, const int32_t* residency, const void* slot_pool,
+                           const rl_route_out* route, const void* scratch, const float* y) {
+  const int rc = check_common(d, layer, x, router_w, residency, route, scratch);
+  if (rc) return rc;
+  if (!slot_pool || !y || !aligned(slot_pool, 256) || !aligned(y, 16)) return RL_E_INVAL;
+  return RL_OK;
+}
+
 extern "C" {
 
 int64_t rl_tensor_bytes(const rl_moe_desc* d) {
@@ -291,9 +301,9 @@ int moe_decode_layer(const rl_moe_desc* d, int32_t layer, const float* x, const 
                      const float* router_bias, const int32_t* residency, const void* slot_pool,
                      const rl_route_out* route, void* scratch, int64_t scratch_bytes, float* y,
                      void* stream) {
-  int rc = check_common(d, layer, x, router_w, residency, route, scratch);
+  const int rc = rl::decode_layer_check(d, layer, x, router_w, residency, slot_pool, route,
+                                        scratch, y);
   if (rc) return rc;
-  if (!slot_pool || !y || !aligned(slot_pool, 256) || !aligned(y, 16)) return RL_E_INVAL;
   const DecodeLayout l = decode_layout(d, 1);
   if (scratch_bytes < l.total) return RL_E_SCRATCH;
   uint8_t* s = static_cast<uint8_t*>(scratch);

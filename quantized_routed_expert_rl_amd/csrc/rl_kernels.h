@@ -107,6 +107,11 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st);
 
+// moe_decode_layer's argument checks, scratch size aside (abi.hip).
+int decode_layer_check(const rl_moe_desc* d, int32_t layer, const float* x, const float* router_w,
+                       const int32_t* residency, const void* slot_pool, const rl_route_out* route,
+                       const void* scratch, const float* y);
+
 void launch_rmsnorm(int T, int H, const float* x, float* out, float eps, hipStream_t st);
 void launch_residual_rmsnorm(int T, int H, const float* x, const float* y,
                              const uint32_t* early_out, float* x_out, float* a_out, float eps,

@@ -153,3 +153,27 @@ def test_driver_argument_checks():
     B.lib.rl_driver_destroy(None)
     cfg = B.RlDriverConfig()                 # every pointer NULL
     assert B.lib.rl_driver_create(C.byref(cfg), None) is None
+
+
+def test_noalloc_decode_argument_checks():
+    """moe_decode_layer_noalloc rejects bad arguments and layers whose decode
+    scratch exceeds its fixed array before any device call (so these run
+    without a GPU)."""
+    out = B.route_out(0x100, 0x100, 0x100, 0x100, 0x100)
+
+    def call(d, x=0x1000, pool=0x1000, y=0x2000, layer=0, route=out):
+        return B.lib.moe_decode_layer_noalloc(C.byref(d), layer, x, 0x1000, None, 0x1000, pool,
+                                              C.byref(route), y, None)
+    real = B.desc(2048, 512, 10, 512, 2, 2, 512)
+    assert B.rl_decode_scratch_bytes(real) == 22528 <= B.RL_NOALLOC_SCRATCH_BYTES
+    big = B.desc(2048, 1024, 32, 2048, 1, 2, 1024)                 # 4 KiB + 256 KiB of scratch
+    assert B.rl_decode_scratch_bytes(big) > B.RL_NOALLOC_SCRATCH_BYTES
+    assert call(big) == B.RL_E_SCRATCH
+    assert call(real, x=None) == B.RL_E_INVAL
+    assert call(real, x=0x1004) == B.RL_E_INVAL
+    assert call(real, pool=None) == B.RL_E_INVAL
+    assert call(real, pool=0x1010) == B.RL_E_INVAL                 # pool not 256-byte aligned
+    assert call(real, y=None) == B.RL_E_INVAL
+    assert call(real, layer=2) == B.RL_E_RANGE
+    assert call(real, route=B.route_out(0x100, None, 0x100, 0x100, 0x100)) == B.RL_E_INVAL
+    assert call(B.desc(300, 512, 10, 512)) == B.RL_E_SHAPE
