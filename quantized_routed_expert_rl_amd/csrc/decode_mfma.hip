@@ -257,18 +257,22 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
   const int rho = lane & 15, q = lane >> 4;
   const int64_t blk = int64_t(i0 + rho / BPT) * KBD + rho % BPT;
   for (int r = wv; r < k; r += nw) {
-    float v[NU][16];
-    if (r == wv) {
-      __builtin_amdgcn_s_waitcnt(0);     // the copy into LDS has landed
-      wave_lds_sync();
-      const float* hf = reinterpret_cast<const float*>(s_hf);
+    if (r != wv) {
+      // a later expert (more experts than waves): its h_r into the wave's
+      // staging region, whose previous contents were read an iteration ago
+      const uint8_t* g = reinterpret_cast<const uint8_t*>(hbuf + int64_t(r) * F) + 16 * lane;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) load_run(hf, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
-    } else {
-      const float* hr = hbuf + int64_t(r) * F;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) load_run(hr, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
+      for (int c = 0; c < KBD; ++c) __builtin_amdgcn_global_load_lds(g + c * 1024, s_hf + c * 1024, 16, 0, 0);
     }
+    // h_r always comes from LDS, so the only global loads in flight while it
+    // is quantised below are this expert's code loads: the quantisation
+    // overlaps them instead of waiting for them at a join of two paths
+    __builtin_amdgcn_s_waitcnt(0);       // the copy into LDS has landed
+    wave_lds_sync();
+    float v[NU][16];
+    const float* hf = reinterpret_cast<const float*>(s_hf);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load_run(hf, lane + 64 * u, lane + 64 * u < 16 * KBD, v[u]);
     const int slot = s_sl[wv][r];
     const uint8_t* td = tensor_base(pv, slot, 2);
     TileCodes cd[NH];

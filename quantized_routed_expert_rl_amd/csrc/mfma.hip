@@ -413,27 +413,10 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st) {
                                                                    a.early_out);
 }
 
-// Compute units of the current device (the expert kernels run one block per
-// compute unit); queried once per device.  Calls from several host threads
-// may query at the same time; they store the same value.
-static int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
   auto kern = a.qbits == 3 ? prefill_expert_kernel<true, 3> : prefill_expert_kernel<true, 2>;
-  kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
+  kern<<<device_cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.xq, a.xe, a.early_out, p.n_tiles,
                                    p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
                                    p.pairs, a.hbuf);
 }
@@ -441,7 +424,7 @@ void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st) {
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st) {
   const PlanPtrs& p = a.plan;
   auto kern = a.qbits == 3 ? prefill_expert_kernel<false, 3> : prefill_expert_kernel<false, 2>;
-  kern<<<cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
+  kern<<<device_cu_count(), 512, 0, st>>>(a.pool, a.H, a.F, a.k, a.hq, a.he, a.early_out, p.n_tiles,
                                    p.tile_bucket, p.tile_start, p.bucket_start, p.bucket_slot,
                                    p.pairs, a.ebuf);
 }

@@ -107,6 +107,9 @@ void launch_quantize_h(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_gateup_mfma(const PrefillArgs& a, hipStream_t st);
 void launch_prefill_down_mfma(const PrefillArgs& a, hipStream_t st);
 
+// Compute units of the current device (cached per device; util.hip).
+int device_cu_count();
+
 // moe_decode_layer's argument checks, scratch size aside (abi.hip).
 int decode_layer_check(const rl_moe_desc* d, int32_t layer, const float* x, const float* router_w,
                        const int32_t* residency, const void* slot_pool, const rl_route_out* route,

@@ -2,10 +2,28 @@
 // the residual add after it, skipped when the layer's early-out flag is set.
 // They are not part of the MoE layer; they let a stack of layers run on the
 // device without host round trips.
+#include <atomic>
+
 #include "rl_common.h"
 #include "rl_kernels.h"
 
 namespace rl {
+
+// Compute units of the current device, queried once per device.  Calls from
+// several host threads may query at the same time; they store the same value.
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // 1 / sqrt(mean(v^2) + eps) of one token's row, from each thread's float64
 // sum of squares, in every thread of the 256-thread block.
