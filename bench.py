@@ -40,8 +40,11 @@ def parse():
                     help="skip the cache-flushed timings and the HBM read ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
+    ap.add_argument("--no-stacks", action="store_true",
+                    help="skip the 48-layer stacks of the default line (decode_48l, prefill_48l 2-bit)")
     ap.add_argument("--stacks", action="store_true",
-                    help="also time the 48-layer stacks (decode_48l, prefill_48l 2-bit and 3-bit)")
+                    help="also time prefill_48l with 3-bit weights and the bounded-pool decode stacks "
+                         "(miss service, prefetch, native driver)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -199,6 +202,42 @@ def main():
                 + w.top_k * w.width * 4)
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     layer_bytes = w.top_k * 3 * tb + w.n_experts * w.hidden * 4 + 2 * w.hidden * 4
+    expert_gu_bytes = w.top_k * 2 * tb               # the ten experts' gate and up codes alone
+
+    # The same launches with the 256 MB Infinity Cache flushed before each one
+    # (a 512 MiB read-modify-write of another buffer).  One graph holds M pairs
+    # (flush, launch i) and another the M flushes alone; the difference of
+    # their replay times over M is the cold time per launch, with the same
+    # back-to-back launch structure as the warm figure (a graph of a single
+    # launch would mostly time the graph's own launch).
+    flush = None if args.no_cold else torch.zeros(512 << 18, device="cuda")
+
+    def cold_per_item_ms(items, reps=5):
+        def cap(with_items):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for it in items:
+                    flush.add_(1.0)
+                    if with_items:
+                        it()
+            g.replay()
+            return g
+        gp, gf = cap(True), cap(False)
+        tp, tf = [], []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                tp.append(event_ms(gp.replay, stream, 1))
+                tf.append(event_ms(gf.replay, stream, 1))
+        del gp, gf
+        return (sorted(tp)[reps // 2] - sorted(tf)[reps // 2]) / len(items)
+
+    gu_cold_ms = None
+    if flush is not None:
+        def gu_launch(t):
+            return lambda: lib.rl_decode_stage(C.byref(d), 1, 0, xp[t], W0, None, res, pool,
+                                               C.byref(outs2[t]), scr[t].data_ptr(), sb_tok, None,
+                                               torch.cuda.current_stream().cuda_stream)
+        gu_cold_ms = cold_per_item_ms([gu_launch(t) for t in range(32)])
 
     line = {
         "metric": METRIC,
@@ -234,6 +273,15 @@ def main():
             "traffic": stored_traffic("decode_topk_gateup"),
             "bytes_per_launch": gu_bytes,
             "us_per_launch": round(gu_ms * 1e3, 3),
+            "expert_bytes_per_launch": expert_gu_bytes,
+            "frac_expert_bytes": round(expert_gu_bytes / (gu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "cold": None if gu_cold_ms is None else {
+                "us_per_launch": round(gu_cold_ms * 1e3, 3),
+                "achieved": round(gu_bytes / (gu_cold_ms * 1e-3) / 1e9, 1),
+                "frac": round(gu_bytes / (gu_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "how": "Infinity Cache flushed (512 MiB read-modify-write) before each of 32 "
+                       "launches: graph of (flush, launch) pairs minus a graph of the flushes alone, "
+                       "HIP events, median of 5"},
         },
     }
 
@@ -316,6 +364,12 @@ def main():
               "down": U * tb3 + P * w3.width * 4 + P * w3.hidden * 4}
         dom = max(stage_ms, key=stage_ms.get)
         ach = gb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        stage_cold_ms = None
+        if flush is not None:
+            stage = 1 if dom == "gateup" else 2
+            stage_cold_ms = cold_per_item_ms(
+                [lambda: B.rl_prefill_stage(m3.desc, stage, 0, T3, w3.plan_cap, X3, m3.residency,
+                                            m3.pool, r3.c(), s3, s3.numel(), Y3)] * 8)
         chunk_bytes = U * 3 * tb3 + w3.n_experts * w3.hidden * 4 + 2 * T3 * w3.hidden * 4
         line["prefill"] = {
             "value": round(T3 / (p_ms * 1e-3), 1),
@@ -335,7 +389,14 @@ def main():
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_GBS, 4),
                          "traffic": stored_traffic("prefill_" + dom),
-                         "bytes_per_launch": gb[dom]},
+                         "bytes_per_launch": gb[dom],
+                         "us_per_launch": round(stage_ms[dom] * 1e3, 2),
+                         "cold": None if stage_cold_ms is None else {
+                             "us_per_launch": round(stage_cold_ms * 1e3, 2),
+                             "achieved": round(gb[dom] / (stage_cold_ms * 1e-3) / 1e9, 1),
+                             "frac": round(gb[dom] / (stage_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "how": "Infinity Cache flushed before each of 8 stage launches (graph "
+                                    "of flush + stage pairs minus the flushes alone)"}},
         }
 
     # ------------------------------------- cold caches and the HBM read ceiling
@@ -345,32 +406,11 @@ def main():
     # and a plain streaming read of 1 GiB gives the ceiling HBM reaches on
     # this box.
     if not args.no_cold:
-        flush = torch.zeros(512 << 18, device="cuda")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-        def cold_ms(fn, reps):
-            tot = 0.0
-            for _ in range(reps):
-                with torch.cuda.stream(stream):
-                    flush.add_(1.0)
-                    e0.record(stream)
-                    fn()
-                    e1.record(stream)
-                e1.synchronize()
-                tot += e0.elapsed_time(e1)
-            return tot / reps
-
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            lib.moe_decode_layer(C.byref(d), 0, xp[0], W0, None, res, pool, C.byref(outs[0]),
-                                 sp, sb, yp[0], stream.cuda_stream)
-        with torch.cuda.graph(g1, stream=stream):
-            lib.moe_decode_layer(C.byref(d), 0, xp[0], W0, None, res, pool, C.byref(outs[0]),
-                                 sp, sb, yp[0], torch.cuda.current_stream().cuda_stream)
-        g1.replay()
-        cold_tok_ms = cold_ms(g1.replay, 32)
-        with torch.cuda.stream(stream):
-            warm_tok_ms = event_ms(g1.replay, stream, 32)   # the same one-token graph, warm
+        def token(t):
+            return lambda: lib.moe_decode_layer(C.byref(d), 0, xp[t], W0, None, res, pool,
+                                                C.byref(outs[t]), sp, sb, yp[t],
+                                                torch.cuda.current_stream().cuda_stream)
+        cold_tok_ms = cold_per_item_ms([token(t) for t in range(32)])
         big = torch.ones(1 << 28, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         with torch.cuda.stream(stream):
@@ -378,13 +418,13 @@ def main():
             read()
             read_ms = event_ms(read, stream, 5)
         cold = {"decode_us_per_token": round(cold_tok_ms * 1e3, 3),
-                "decode_us_per_token_same_graph_warm": round(warm_tok_ms * 1e3, 3),
                 "decode_tokens_per_s": round(1e3 / cold_tok_ms, 1),
+                "how": "Infinity Cache flushed before each of 32 tokens (graph of flush + token "
+                       "pairs minus the flushes alone)",
                 "hbm_read_ceiling_gbs": round(big.numel() * 4 / (read_ms * 1e-3) / 1e9, 1),
                 "read_ceiling_kernel": "rl_stream_read over 1 GiB"}
         if not args.no_prefill:
-            gp = graph_of(chunk)
-            cold_chunk_ms = cold_ms(gp.replay, 5)
+            cold_chunk_ms = cold_per_item_ms([chunk] * 8)
             cold["prefill_ms_per_chunk"] = round(cold_chunk_ms, 4)
             cold["prefill_tokens_per_s"] = round(T3 / (cold_chunk_ms * 1e-3), 1)
         line["cold"] = cold
@@ -392,7 +432,9 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ stacks
-    if args.stacks:
+    # decode_48l and prefill_48l (2-bit) by default; 3-bit prefill and the
+    # bounded-pool decode stacks with --stacks
+    if args.stacks or not args.no_stacks:
         from quantized_routed_expert_rl_amd.stack import DecodeStack, PrefillStack
         stacks = {}
         wd = workloads.get("decode_48l")
@@ -419,9 +461,9 @@ def main():
             "layers": wd.n_layers, "flagged_layers_last_token": int(flags.sum()),
             "workload": "256 sequential tokens through 48 decode layers, Zipf-biased routing, "
                         "4608 of 24576 experts resident; one HIP graph per token"}
-        del md, ds
+        del gd, md, ds
         torch.cuda.empty_cache()
-        for qb in (2, 3):
+        for qb in ((2, 3) if args.stacks else (2,)):
             wp = workloads.get("prefill_48l", qb)
             mp_ = DeviceModel(wp)
             ps = PrefillStack(mp_, wp.chunks, wp.plan_cap)
@@ -442,6 +484,7 @@ def main():
                             f"Zipf-biased routing, all experts resident, {qb}-bit block weights"}
             del mp_, ps
             torch.cuda.empty_cache()
+    if args.stacks:
         # decode with a bounded pool (each layer's 224 most popular experts
         # resident) and miss service, without and with the pre-gated prefetch
         from quantized_routed_expert_rl_amd.stack import (HostExpertStore, NativeServicedDecode,
@@ -490,6 +533,7 @@ def main():
             del sv, mh
             torch.cuda.empty_cache()
         del store
+    if args.stacks or not args.no_stacks:
         line["stacks"] = stacks
 
     # -------------------------------------------------------- cpu oracle
@@ -516,9 +560,11 @@ def main():
                 O.decode_layer(shape, xs[n1], Wr, None, model.table[0], lambda s: host_pool[s])
                 n1 += 1
             cdt1 = time.perf_counter() - t1
+        cpu_model = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                          if l.startswith("model name")), "unknown")
         line["cpu_baseline"] = {
             "value": round(n / cdt, 3), "unit": "tokens/s", "cores": max(blas + [1]),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "logical_cpus": os.cpu_count(),
             "sample": f"first {n} of the {T} decode_1l tokens through oracle.decode_layer "
                       f"({cdt:.1f} s); float64 NumPy, BLAS threads {max(blas + [1])}, "
                       f"host has {os.cpu_count()} logical CPUs",
