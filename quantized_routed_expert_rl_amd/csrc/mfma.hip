@@ -116,16 +116,39 @@ struct RowCodes {                  // one lane's share of a row's 256-value bloc
   uint4 hb;                        // third code bit of the 128 codes (3-bit only)
 };
 
+// Buffer loads of a lane's block: the slot's buffer descriptor lives in
+// scalar registers (one per item: gate/up tiles read two tensors of the slot,
+// so the descriptor covers the slot and the lane's tensor is part of its
+// offset), the lane's part of each address (its tensor, row and half) is a
+// per-lane offset fixed for the whole kernel, and the block index's
+// wave-uniform part is a scalar offset, so no per-lane address arithmetic
+// runs per step.  Block blk = bu + bl: bu (uniform) = ROWS*tile*KB + kb,
+// bl (lane) = rowoff*KB; bu + bl is even whenever bl is odd (KB = 1, where
+// bu = ROWS*tile is even), so blk/2 = bu/2 + bl/2 for the d plane.
+struct LaneOffsets {
+  int q, s, d, hb;                 // per-lane byte offsets inside the tensor
+};
+
+__device__ inline LaneOffsets lane_offsets(const PoolView& p, int which, int bl, int h) {
+  const int t = which * int(p.tensor_bytes);
+  LaneOffsets o;
+  o.q = t + int(p.q) + 64 * bl + 32 * h;
+  o.s = t + int(p.s) + 4 * bl;
+  o.d = t + int(p.d) + 4 * (bl >> 1);
+  o.hb = t + int(p.hb) + 32 * bl + 16 * h;
+  return o;
+}
+
 template <int QBITS>
-__device__ inline RowCodes load_row_codes(const uint8_t* t, const PoolView& p, int64_t blk,
-                                          int h) {
+__device__ inline RowCodes load_row_codes(__amdgpu_buffer_rsrc_t t, const LaneOffsets& o, int bu) {
   RowCodes r;
-  r.lo = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h);
-  r.hi = *reinterpret_cast<const uint4*>(t + p.q + 64 * blk + 32 * h + 16);
-  r.s = *reinterpret_cast<const uint32_t*>(t + p.s + 4 * blk);
-  r.dh = *reinterpret_cast<const uint32_t*>(t + p.d + 4 * (blk >> 1));
+  r.lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, o.q, 64 * bu, 0));
+  r.hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, o.q, 64 * bu + 16, 0));
+  r.s = __builtin_amdgcn_raw_buffer_load_b32(t, o.s, 4 * bu, 0);
+  r.dh = __builtin_amdgcn_raw_buffer_load_b32(t, o.d, 4 * (bu >> 1), 0);
   r.hb = make_uint4(0u, 0u, 0u, 0u);
-  if (QBITS == 3) r.hb = *reinterpret_cast<const uint4*>(t + p.hb + 32 * blk + 16 * h);
+  if (QBITS == 3)
+    r.hb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, o.hb, 32 * bu, 0));
   return r;
 }
 
@@ -228,11 +251,17 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
   // which would make the compiler copy the ring and wait for it).
   int s_item = r0 / RPI, s_tile = (r0 - s_item * RPI) * 8 + w, s_kb = 0, s_left = NQ;
   // the item's tensor in its bucket's pool slot
-  auto item_tensor = [&](int it) { return tensor_base(pv, bucket_slot[item_bucket[it]], which); };
-  const uint8_t* s_t = item_tensor(s_item);
+  // the item's pool slot as a buffer descriptor (reads past the slot's end
+  // return 0)
+  auto item_tensor = [&](int it) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(tensor_base(pv, bucket_slot[item_bucket[it]], 0)), 0,
+        int(pv.slot_bytes), 0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t s_t = item_tensor(s_item);
+  const LaneOffsets lo = lane_offsets(pv, which, rowoff * KB, h);
   auto next_codes = [&]() {
-    const RowCodes rc =
-        load_row_codes<QBITS>(s_t, pv, int64_t(ROWS * s_tile + rowoff) * KB + s_kb, h);
+    const RowCodes rc = load_row_codes<QBITS>(s_t, lo, ROWS * s_tile * KB + s_kb);
     if (--s_left <= 0) return rc;
     if (++s_kb == KB) {
       s_kb = 0;
