@@ -214,12 +214,11 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
 // [0, n_slots) mean not resident (-1).
 __device__ inline int slot_of(int v, int n_slots) { return (v >= 0 && v < n_slots) ? v : -1; }
 
-// Weights, slots and miss count of one token from the selection in LDS
-// (sel_res: the selected experts' residency entries).  Returns the token's
-// miss count (in every lane).
-__device__ __forceinline__ int finish_token(const int* sel_ids, const float* sel_lg, const int* sel_res,
-                                   int k, int E, int n_slots, int32_t* ids, float* weights,
-                                   int32_t* slots) {
+// Renormalised softmax weight of the lane's rank (lanes < k) from the
+// selected logits in LDS, sel_lg[0] the largest: exp(l_r - l_0) over their
+// sum in rank order, in float64.  Every block that needs the weights calls
+// this, so they agree bit for bit.
+__device__ __forceinline__ float selected_weight(const float* sel_lg, int k) {
   const int lane = threadIdx.x & 63;
   double a = 0.0;
   if (lane < k) a = exp(double(sel_lg[lane]) - double(sel_lg[0]));
@@ -231,12 +230,23 @@ __device__ __forceinline__ int finish_token(const int* sel_ids, const float* sel
     total += __longlong_as_double((static_cast<long long>(hi) << 32) |
                                   static_cast<unsigned int>(lo));
   }
+  return float(a / total);
+}
+
+// Weights, slots and miss count of one token from the selection in LDS
+// (sel_res: the selected experts' residency entries).  Returns the token's
+// miss count (in every lane).
+__device__ __forceinline__ int finish_token(const int* sel_ids, const float* sel_lg, const int* sel_res,
+                                   int k, int E, int n_slots, int32_t* ids, float* weights,
+                                   int32_t* slots) {
+  const int lane = threadIdx.x & 63;
+  const float w = selected_weight(sel_lg, k);
   int slot = -1;
   if (lane < k) {
     const int e = min(max(sel_ids[lane], 0), E - 1);   // in bounds even for NaN logits
     slot = slot_of(sel_res[lane], n_slots);
     ids[lane] = e;
-    weights[lane] = float(a / total);
+    weights[lane] = w;
     slots[lane] = slot;
   }
   return __popcll(__ballot(lane < k && slot < 0));
