@@ -314,6 +314,11 @@ int rl_residual_rmsnorm(int32_t n_tokens, int32_t hidden, const float* x, const 
  *   number of loads (>= 0), RL_E_RANGE (bad layer/id, k < 1, or more misses
  *   than slots outside the selection: the cache is then unchanged) or
  *   RL_E_INVAL (NULL pointer, or a reservation already open).
+ * rl_cache_reserve_excluding: rl_cache_reserve that takes no victim from a
+ *   slot holding an expert of exclude_layer (-1: none excluded), for loads
+ *   queued while that layer may still be running: its kernels read only its
+ *   own experts' slots.  Returns RL_E_RANGE (cache unchanged, counted as an
+ *   abort) when too few slots qualify (decided before anything changes).
  * rl_cache_touch: the resident ones of a layer's k ids become the most
  *   recently used (the first id most recent), as after the device used them
  *   without any load; returns how many were resident, RL_E_RANGE for a bad
@@ -335,6 +340,9 @@ int rl_cache_insert(rl_cache* c, int32_t layer, int32_t expert, int32_t slot);
 int32_t rl_cache_lookup(const rl_cache* c, int32_t layer, int32_t expert);
 int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, int32_t* slots,
                      int32_t* load, int32_t* evicted, uint32_t* gens);
+int rl_cache_reserve_excluding(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k,
+                               int32_t exclude_layer, int32_t* slots, int32_t* load,
+                               int32_t* evicted, uint32_t* gens);
 int rl_cache_touch(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k);
 int rl_cache_commit(rl_cache* c);
 int rl_cache_abort(rl_cache* c);
@@ -355,10 +363,16 @@ int rl_cache_stats(const rl_cache* c, int64_t* out);
  * Host code driving the library's own calls: per layer moe_decode_layer on
  * a_l = rmsnorm(x_l), then rl_residual_rmsnorm (x_{l+1} = x_l + y_l, or x_l
  * when the layer's flag is set), replayed as HIP graphs captured at creation.
- * Misses are copied from the host store into the slots the cache picks
- * (hipMemcpyAsync on the stream) and the changed residency entries follow;
+ * A layer's misses are copied from the host store into the slots the cache
+ * picks by one gather launch that reads the store through its device
+ * address and also writes the changed residency entries (one hipMemcpyAsync
+ * per expert plus an entry copy when the store has no device address);
  * after a token every layer's selection is touched in the cache ("Red Lite
- * dev21", "What changed", LRU stamps refreshed after the token).
+ * dev21", "What changed", LRU stamps refreshed after the token).  With
+ * prefetch, layer l's graph also runs layer l+2's router on layer l+1's
+ * input; the host reserves those experts (no victim among layer l+1's slots)
+ * and their gather is queued right behind layer l+1's graph, so the copies
+ * run while the host reads layer l+1's flags and relaunches.
  *
  * rl_driver_config (host struct; the pointers stay owned by the caller and
  * must outlive the driver):
@@ -380,7 +394,8 @@ int rl_cache_stats(const rl_cache* c, int64_t* out);
  *   early_out_limit  >= 0: a token with more early-outs than this sends the
  *                    next tokens to the layer-by-layer path
  *   prefetch         nonzero: predict and load the next layer's experts on
- *                    the layer-by-layer path
+ *                    the layer-by-layer path (needs a host_store with a
+ *                    device address: rl_driver_create returns NULL otherwise)
  *   eps              RMSNorm epsilon
  * rl_driver_create: allocates its device and pinned buffers, captures its
  *   graphs on `stream` (a hipStream_t) and runs one layer eagerly; NULL on a

@@ -91,6 +91,9 @@ _SIGS = {
     "rl_cache_lookup": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32]),
     "rl_cache_reserve": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rl_cache_reserve_excluding": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+                                             C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]),
     "rl_cache_touch": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32]),
     "rl_cache_commit": (C.c_int, [C.c_void_p]),
     "rl_cache_abort": (C.c_int, [C.c_void_p]),
@@ -296,8 +299,11 @@ class ExpertCache:
     def lookup(self, layer: int, expert: int) -> int:
         return lib.rl_cache_lookup(self.h, layer, expert)
 
-    def reserve(self, layer: int, ids):
-        """-> (n_loads, slots, load, evicted, gens) as numpy arrays; raises on error."""
+    def reserve(self, layer: int, ids, exclude_layer: int = -1, raw: bool = False):
+        """-> (n_loads, slots, load, evicted, gens) as numpy arrays; raises on
+        error, or with ``raw`` returns the error code in n_loads.
+        ``exclude_layer`` >= 0: rl_cache_reserve_excluding (no victim holds an
+        expert of that layer)."""
         import numpy as np
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         k = ids.size
@@ -305,9 +311,15 @@ class ExpertCache:
         load = np.empty(k, np.int32)
         evicted = np.empty(k, np.int32)
         gens = np.empty(k, np.uint32)
-        n = lib.rl_cache_reserve(self.h, layer, ids.ctypes.data, k, slots.ctypes.data,
-                                 load.ctypes.data, evicted.ctypes.data, gens.ctypes.data)
-        check(min(n, 0), "rl_cache_reserve")
+        if exclude_layer >= 0:
+            n = lib.rl_cache_reserve_excluding(self.h, layer, ids.ctypes.data, k, exclude_layer,
+                                               slots.ctypes.data, load.ctypes.data,
+                                               evicted.ctypes.data, gens.ctypes.data)
+        else:
+            n = lib.rl_cache_reserve(self.h, layer, ids.ctypes.data, k, slots.ctypes.data,
+                                     load.ctypes.data, evicted.ctypes.data, gens.ctypes.data)
+        if not raw:
+            check(min(n, 0), "rl_cache_reserve")
         return n, slots, load, evicted, gens
 
     def touch(self, layer: int, ids) -> int:

@@ -30,6 +30,7 @@ struct rl_cache {
   std::vector<int32_t> prev, next;    // recency list, -1 ends it
   std::vector<uint8_t> pinned;
   std::vector<uint32_t> gen;          // loads into each slot so far
+  std::vector<int32_t> per_layer;     // resident experts of each layer
   int32_t head = -1, tail = -1;
   // the open reservation: pinned slots in order, and (slot, previous key, new key) of each load
   std::vector<int32_t> held;
@@ -72,7 +73,11 @@ void rollback(rl_cache* c) {
   for (auto it = c->loads.rbegin(); it != c->loads.rend(); ++it) {
     c->slot_of_key[it->new_key] = -1;
     c->key_of_slot[it->slot] = it->old_key;
-    if (it->old_key >= 0) c->slot_of_key[it->old_key] = it->slot;
+    c->per_layer[it->new_key / c->n_experts] -= 1;
+    if (it->old_key >= 0) {
+      c->slot_of_key[it->old_key] = it->slot;
+      c->per_layer[it->old_key / c->n_experts] += 1;
+    }
   }
   for (auto it = c->held.rbegin(); it != c->held.rend(); ++it) {
     c->pinned[*it] = 0;
@@ -103,6 +108,7 @@ rl_cache* rl_cache_create(int32_t n_slots, int32_t n_layers, int32_t n_experts) 
   c->next.assign(n_slots, -1);
   c->pinned.assign(n_slots, 0);
   c->gen.assign(n_slots, 0);
+  c->per_layer.assign(n_layers, 0);
   for (int32_t s = 0; s < n_slots; ++s) push_head(c, s);   // slot 0 least recent: used first
   return c;
 }
@@ -117,6 +123,7 @@ int rl_cache_insert(rl_cache* c, int32_t layer, int32_t expert, int32_t slot) {
   if (c->slot_of_key[key] >= 0 || c->key_of_slot[slot] >= 0) return RL_E_INVAL;
   c->slot_of_key[key] = slot;
   c->key_of_slot[slot] = key;
+  c->per_layer[layer] += 1;
   unlink(c, slot);
   push_head(c, slot);
   return RL_OK;
@@ -129,6 +136,12 @@ int32_t rl_cache_lookup(const rl_cache* c, int32_t layer, int32_t expert) {
 
 int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, int32_t* slots,
                      int32_t* load, int32_t* evicted, uint32_t* gens) {
+  return rl_cache_reserve_excluding(c, layer, ids, k, -1, slots, load, evicted, gens);
+}
+
+int rl_cache_reserve_excluding(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k,
+                               int32_t exclude_layer, int32_t* slots, int32_t* load,
+                               int32_t* evicted, uint32_t* gens) {
   if (!c || !ids || !slots || !load || !evicted) return RL_E_INVAL;
   if (!c->held.empty()) return RL_E_INVAL;            // commit or abort the previous one first
   if (layer < 0 || layer >= c->n_layers || k < 1) return RL_E_RANGE;
@@ -136,7 +149,8 @@ int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, 
     if (ids[i] < 0 || ids[i] >= c->n_experts) return RL_E_RANGE;
   c->stats[0] += 1;
   // refuse, changing nothing, a selection with more distinct misses than
-  // slots outside its distinct hits
+  // slots that may be victims: outside its distinct hits and not holding an
+  // expert of exclude_layer (the hits are the layer's own experts)
   int32_t n_hit = 0, n_miss = 0;
   for (int32_t i = 0; i < k; ++i) {
     bool repeat = false;
@@ -144,7 +158,12 @@ int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, 
     if (repeat) continue;
     if (c->slot_of_key[size_t(layer) * c->n_experts + ids[i]] >= 0) ++n_hit; else ++n_miss;
   }
-  if (n_miss > c->n_slots - n_hit) {
+  int32_t n_victims = c->n_slots - n_hit;
+  if (exclude_layer == layer)
+    n_victims = c->n_slots - c->per_layer[layer];
+  else if (exclude_layer >= 0 && exclude_layer < c->n_layers)
+    n_victims -= c->per_layer[exclude_layer];
+  if (n_miss > n_victims) {
     c->stats[4] += 1;
     return RL_E_RANGE;
   }
@@ -174,8 +193,11 @@ int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, 
       slots[i] = again;
       continue;
     }
-    const int32_t v = c->tail;                        // least recently used, unpinned
-    if (v < 0) {                                      // every slot is held by this selection
+    // least recently used, unpinned, and not holding an expert of exclude_layer
+    int32_t v = c->tail;
+    while (v >= 0 && c->key_of_slot[v] >= 0 && c->key_of_slot[v] / c->n_experts == exclude_layer)
+      v = c->prev[v];
+    if (v < 0) {                                      // not reached: counted above
       rollback(c);
       c->stats[4] += 1;
       return RL_E_RANGE;
@@ -186,8 +208,10 @@ int rl_cache_reserve(rl_cache* c, int32_t layer, const int32_t* ids, int32_t k, 
     const int32_t old = c->key_of_slot[v];
     if (old >= 0) {
       c->slot_of_key[old] = -1;
+      c->per_layer[old / c->n_experts] -= 1;
       c->stats[3] += 1;
     }
+    c->per_layer[layer] += 1;
     c->loads.push_back({v, old, key});
     c->key_of_slot[v] = key;
     c->slot_of_key[key] = v;

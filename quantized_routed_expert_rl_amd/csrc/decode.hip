@@ -47,9 +47,13 @@ template <int RPB, int NM>
 __global__ __launch_bounds__(64) void decode_router_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
     int E, int H, int rows, float* __restrict__ logits, float* __restrict__ logits_out,
-    const uint32_t* __restrict__ early_out, int sticky) {
-  if (sticky && *early_out) return;
+    const uint32_t* __restrict__ early_out, int sticky, uint32_t* clear0, uint32_t* clear1) {
   const int lane = threadIdx.x;
+  if (blockIdx.x == 0 && lane == 0) {   // a one-token rl_route's miss count and flag
+    if (clear0) *clear0 = 0u;
+    if (clear1) *clear1 = 0u;
+  }
+  if (sticky && *early_out) return;
   const int e0 = blockIdx.x * rows;
   float4 xv[NM];
 #pragma unroll
@@ -285,7 +289,8 @@ static void router_rpb(const DecodeArgs& a, int rows, hipStream_t st) {
   case 256 * NM:                                                                      \
     decode_router_kernel<RPB, NM><<<grid, 64, 0, st>>>(a.x, a.W, a.bias, a.E, a.H,    \
                                                        rows, a.logits, a.logits_out,  \
-                                                       a.early_out, int(a.sticky));   \
+                                                       a.early_out, int(a.sticky),    \
+                                                       a.clear_miss, a.clear_flag);   \
     break;
     RL_CASE(1) RL_CASE(2) RL_CASE(4) RL_CASE(8)
 #undef RL_CASE

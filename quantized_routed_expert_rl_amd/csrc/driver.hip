@@ -17,9 +17,19 @@
 //    synchronous path (one launch and one wait per layer, a miss serviced as
 //    soon as its layer shows it), and a token that needed no load sends them
 //    back;
-//  - pre-gated prefetch (synchronous path, optional): layer l+1's router on
-//    layer l's input, in layer l's graph, predicts l+1's selection, and the
-//    predicted experts are reserved and copied ahead of layer l+1;
+//  - pre-gated prefetch (synchronous path, optional): layer m's router on
+//    layer m-1's input predicts m's selection.  Layer l's graph ends with
+//    a_{l+1}, so it also runs layer l+2's router on it and copies the
+//    prediction out with the flags: after the one wait per layer the host
+//    reserves the predicted experts with no victim among layer l+1's slots
+//    (rl_cache_reserve_excluding: a layer reads only its own experts' slots)
+//    and keeps their loads (store rows, slots, table entries).  Right after
+//    layer l+1's graph, behind the event the host waits on, one gather launch
+//    copies them from the store (through its device address): the copies
+//    run while the host wakes, reads the flags and launches the next graph,
+//    time in which the device would otherwise be idle, and the stream orders
+//    them before layer l+2 and before any miss service.  Layer 1's
+//    prediction is made from a_0 before layer 0;
 //  - after the token every layer's selection becomes the most recently used
 //    ("Red Lite dev21 - GPU-routed decode", "What changed": LRU stamps
 //    refreshed after the token).
@@ -28,9 +38,10 @@
 // fully resident stack.
 //
 // Graphs (captured once at creation): suffix[l] = layers l .. L-1, single[l]
-// = layer l, single_pf[l] = the prediction for l+1 and layer l.  Each ends by
-// copying the flags, miss counts, selected ids (and predicted ids) into pinned
-// host mirrors, so one wait after a launch gives the host all it reads.
+// = layer l; with prefetch, single_pf[l] = layer l then the prediction for
+// l+2 (l+2 < L) and first_pf = the prediction for layer 1 alone.  Each ends
+// by copying the flags, miss counts, selected ids and predicted ids into
+// pinned host mirrors, so one wait after a launch gives the host all it reads.
 // A layer = moe_decode_layer(a_l) -> y_l, then rl_residual_rmsnorm(x_l, y_l,
 // flag) -> x_{l+1}, a_{l+1}; the token starts with x_0 = x0, a_0 = rmsnorm(x0).
 #include <hip/hip_runtime.h>
@@ -51,10 +62,12 @@ struct rl_decode_driver {
   int limit = 0;
   float eps = 0.f;
   hipStream_t st = nullptr;
+  hipEvent_t ev_done = nullptr;
   std::vector<const float*> W, bias;
   int32_t* residency = nullptr;
   uint8_t* pool = nullptr;
   const uint8_t* store = nullptr;
+  const void* store_dev = nullptr;    // the store's device address (gather launches), or NULL
   int64_t slot_bytes = 0;
   rl_cache* cache = nullptr;
   float* x = nullptr;     // caller's [(L+1) x H]
@@ -71,8 +84,10 @@ struct rl_decode_driver {
   uint32_t *h_flags = nullptr, *h_miss = nullptr;
   int32_t *h_ids = nullptr, *h_pids = nullptr, *h_table = nullptr;
   int32_t *h_pairs = nullptr, *d_pairs = nullptr;   // changed table entries (key, slot)
+  rl::ExpertLoads pf;                 // prefetch loads for the next gather launch
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> suffix, single, single_pf;
+  hipGraphExec_t first_pf = nullptr;
   // tokens, early_outs, loads, sync_tokens, evictions, predictions,
   // predicted_selected, prefetch_loads
   int64_t stats[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -125,9 +140,12 @@ int run_mirror(rl_decode_driver* v) {
              : RL_E_DEVICE;
 }
 
+// Layers l0 .. l1-1, then (predict) layer l1+1's router on a_{l1}, then the
+// mirror copy.
 int run_body(rl_decode_driver* v, int l0, int l1, bool predict) {
-  int rc = predict ? run_predict(v, l0) : RL_OK;
+  int rc = RL_OK;
   for (int l = l0; l < l1 && !rc; ++l) rc = run_layer(v, l);
+  if (!rc && predict) rc = run_predict(v, l1);
   return rc ? rc : run_mirror(v);
 }
 
@@ -145,9 +163,28 @@ int capture(rl_decode_driver* v, int l0, int l1, bool predict, hipGraphExec_t* o
   return hipGraphInstantiate(out, g, nullptr, nullptr, 0) == hipSuccess ? RL_OK : RL_E_DEVICE;
 }
 
+// Waits for an event by polling it: the host learns a layer's flags a few
+// microseconds after the device is done, where a blocking wait sleeps and is
+// woken tens of microseconds later.  Every token waits once per layer (and
+// once more per layer with prefetch), so the wake-up latency would be paid
+// dozens of times per token.
+int spin_wait(hipEvent_t e) {
+  for (;;) {
+    const hipError_t r = hipEventQuery(e);
+    if (r == hipSuccess) return RL_OK;
+    if (r != hipErrorNotReady) return RL_E_DEVICE;
+  }
+}
+
+// Everything queued on the main stream so far is done.
+int wait_main(rl_decode_driver* v) {
+  if (hipEventRecord(v->ev_done, v->st) != hipSuccess) return RL_E_DEVICE;
+  return spin_wait(v->ev_done);
+}
+
 int launch_wait(rl_decode_driver* v, hipGraphExec_t g) {
   if (hipGraphLaunch(g, v->st) != hipSuccess) return RL_E_DEVICE;
-  return hipStreamSynchronize(v->st) == hipSuccess ? RL_OK : RL_E_DEVICE;
+  return wait_main(v);
 }
 
 int clear_flags(rl_decode_driver* v, int miss_from) {
@@ -158,50 +195,72 @@ int clear_flags(rl_decode_driver* v, int miss_from) {
   return e == hipSuccess ? RL_OK : RL_E_DEVICE;
 }
 
-// Sends the n changed table entries staged in h_pairs to the device table
-// (one copy and one scatter launch).  The staging stays unchanged until the
-// copy has run: every path waits on the stream before the next load.
-int put_entries(rl_decode_driver* v, int n) {
+// Sends the n changed table entries staged in hp to the device table (dp; one
+// copy and one scatter launch on stream s).  The staging stays unchanged until
+// the copy has run: every load is followed by a wait on the stream.
+int put_entries(rl_decode_driver* v, const int32_t* hp, int32_t* dp, int n, hipStream_t s) {
   if (n == 0) return RL_OK;
-  if (hipMemcpyAsync(v->d_pairs, v->h_pairs, sizeof(int32_t) * 2 * n, hipMemcpyHostToDevice,
-                     v->st) != hipSuccess)
+  if (hipMemcpyAsync(dp, hp, sizeof(int32_t) * 2 * n, hipMemcpyHostToDevice, s) != hipSuccess)
     return RL_E_DEVICE;
-  rl::launch_table_scatter(v->residency, v->d_pairs, n, v->st);
+  rl::launch_table_scatter(v->residency, dp, n, s);
   return hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVICE;
 }
 
-// Reserves layer's selection in the cache and queues the copies of its
-// missing experts from the host store, and the table entries that change.
-// Returns the number of loads (>= 0) or an error; slots and gens receive the
-// selection's slots and their load generations.
-int load_layer(rl_decode_driver* v, int layer, const int32_t* sel, int32_t* slots,
-               uint32_t* gens) {
+// Reserves layer's selection in the cache (no victim among exclude_layer's
+// experts when >= 0) and, with list NULL, queues on stream s the copies of
+// its missing experts from the host store and the table entries that change
+// (through the gather kernel, or memcpys and hp/dp staging); with a list,
+// writes them there for a later gather launch instead.  Returns the number
+// of loads (>= 0) or an error; slots and gens receive the selection's slots
+// and their load generations.
+int load_layer(rl_decode_driver* v, int layer, const int32_t* sel, int32_t* slots, uint32_t* gens,
+               int exclude_layer, hipStream_t s, int32_t* hp, int32_t* dp,
+               rl::ExpertLoads* list = nullptr) {
   const int k = v->k;
   int32_t load[32], evicted[32];
-  const int n = rl_cache_reserve(v->cache, layer, sel, k, slots, load, evicted, gens);
+  const int n = rl_cache_reserve_excluding(v->cache, layer, sel, k, exclude_layer, slots, load,
+                                           evicted, gens);
   if (n < 0) return n;
   int np = 0;
+  rl::ExpertLoads ld;
   for (int i = 0; i < k; ++i) {
     if (!load[i]) continue;
     const int64_t key = int64_t(layer) * v->E + sel[i];
-    if (hipMemcpyAsync(v->pool + int64_t(slots[i]) * v->slot_bytes, v->store + key * v->slot_bytes,
-                       v->slot_bytes, hipMemcpyHostToDevice, v->st) != hipSuccess) {
+    if (v->store_dev) {                      // copied by the gather launch below
+      ld.src_row[ld.n] = key;
+      ld.dst_slot[ld.n] = slots[i];
+      ld.n += 1;
+    } else if (hipMemcpyAsync(v->pool + int64_t(slots[i]) * v->slot_bytes,
+                              v->store + key * v->slot_bytes, v->slot_bytes,
+                              hipMemcpyHostToDevice, s) != hipSuccess) {
       rl_cache_abort(v->cache);
       return RL_E_DEVICE;
     }
     v->h_table[key] = slots[i];
-    v->h_pairs[2 * np] = int32_t(key);
-    v->h_pairs[2 * np + 1] = slots[i];
+    hp[2 * np] = int32_t(key);
+    hp[2 * np + 1] = slots[i];
     np += 1;
     if (evicted[i] >= 0) {
       v->h_table[evicted[i]] = -1;
-      v->h_pairs[2 * np] = evicted[i];
-      v->h_pairs[2 * np + 1] = -1;
+      hp[2 * np] = evicted[i];
+      hp[2 * np + 1] = -1;
       np += 1;
       v->stats[4] += 1;
     }
   }
-  const int rc = put_entries(v, np);
+  int rc = RL_OK;
+  if (list) {                                // a later gather launch does it
+    ld.n_pairs = np;
+    for (int j = 0; j < 2 * np; ++j) ld.pairs[j] = hp[j];
+    *list = ld;
+  } else if (v->store_dev) {                 // copies and table entries in one launch
+    ld.n_pairs = np;
+    for (int j = 0; j < 2 * np; ++j) ld.pairs[j] = hp[j];
+    rl::launch_expert_gather(v->store_dev, v->pool, v->slot_bytes, ld, v->residency, s);
+    rc = hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVICE;
+  } else {
+    rc = put_entries(v, hp, dp, np, s);
+  }
   if (rc) {
     rl_cache_abort(v->cache);
     return rc;
@@ -210,17 +269,30 @@ int load_layer(rl_decode_driver* v, int layer, const int32_t* sel, int32_t* slot
   return n;
 }
 
-// Loads layer f's missing experts and runs layer f again; afterwards its
-// flag must be clear and no slot it used may have been reloaded.
-int service(rl_decode_driver* v, int f) {
+// The predicted experts of layer (layer - 1 runs next): reserved with no
+// victim among layer - 1's slots, their loads kept in v->pf for the gather
+// launched behind layer - 1's graph; a reservation refused for want of such
+// slots loads nothing.  Returns the loads or an error.
+int prefetch_layer(rl_decode_driver* v, int layer, const int32_t* sel) {
+  int32_t slots[32], pairs[4 * 32];
+  uint32_t gens[32];
+  const int n = load_layer(v, layer, sel, slots, gens, layer - 1, v->st, pairs, nullptr, &v->pf);
+  return n == RL_E_RANGE ? 0 : n;
+}
+
+// Loads layer f's missing experts and runs layer f again (graph g: single[f],
+// or single_pf[f], which recomputes the prediction from the finished
+// a_{f+1}); afterwards its flag must be clear and no slot it used may have
+// been reloaded.
+int service(rl_decode_driver* v, int f, hipGraphExec_t g) {
   int32_t sel[32], slots[32];
   uint32_t gens[32];
   for (int i = 0; i < v->k; ++i) sel[i] = v->h_ids[f * v->k + i];
-  const int n = load_layer(v, f, sel, slots, gens);
+  const int n = load_layer(v, f, sel, slots, gens, -1, v->st, v->h_pairs, v->d_pairs);
   if (n < 0) return n;
   v->stats[2] += n;
   int rc = clear_flags(v, v->L);
-  if (!rc) rc = launch_wait(v, v->single[f]);
+  if (!rc) rc = launch_wait(v, g);
   if (rc) return rc;
   if (v->h_flags[v->sticky ? 0 : f] != 0) return RL_E_STATE;
   for (int i = 0; i < v->k; ++i)
@@ -253,26 +325,39 @@ int token(rl_decode_driver* v, const float* x0) {
         if (f < 0) break;
       }
       n_eo += 1;
-      if ((rc = service(v, f))) return rc;
+      if ((rc = service(v, f, v->single[f]))) return rc;
       l = f + 1;
     } else {
-      const bool predict = v->prefetch && l + 1 < L;
-      if ((rc = clear_flags(v, L)) ||
-          (rc = launch_wait(v, predict ? v->single_pf[l] : v->single[l])))
-        return rc;
-      if (v->h_flags[v->sticky ? 0 : l] != 0) {
-        n_eo += 1;
-        if ((rc = service(v, l))) return rc;
-      }
-      if (predict) {                           // queued ahead of layer l+1
+      // the predicted experts of layer m, copied behind layer m-1's graph
+      auto prefetch = [&](int m) {
         std::vector<int32_t> p(v->h_pids, v->h_pids + k);
-        int32_t slots[32];
-        uint32_t gens[32];
-        const int n = load_layer(v, l + 1, p.data(), slots, gens);
+        const int n = prefetch_layer(v, m, p.data());
         if (n < 0) return n;
         v->stats[7] += n;
-        predicted.emplace_back(l + 1, std::move(p));
+        predicted.emplace_back(m, std::move(p));
+        return int(RL_OK);
+      };
+      if (l == 0 && v->prefetch && L > 1) {    // layer 1's prediction, from a_0
+        if ((rc = launch_wait(v, v->first_pf)) || (rc = prefetch(1))) return rc;
       }
+      const bool predict = v->prefetch && l + 2 < L;
+      hipGraphExec_t g = predict ? v->single_pf[l] : v->single[l];
+      if ((rc = clear_flags(v, L))) return rc;
+      if (hipGraphLaunch(g, v->st) != hipSuccess ||
+          hipEventRecord(v->ev_done, v->st) != hipSuccess)
+        return RL_E_DEVICE;
+      if (v->pf.n > 0 || v->pf.n_pairs > 0) {  // layer l+1's predicted experts
+        rl::launch_expert_gather(v->store_dev, v->pool, v->slot_bytes, v->pf, v->residency,
+                                 v->st);
+        v->pf.n = v->pf.n_pairs = 0;
+        if (hipGetLastError() != hipSuccess) return RL_E_DEVICE;
+      }
+      if ((rc = spin_wait(v->ev_done))) return rc;
+      if (v->h_flags[v->sticky ? 0 : l] != 0) {
+        n_eo += 1;
+        if ((rc = service(v, l, g))) return rc;
+      }
+      if (predict && (rc = prefetch(l + 2))) return rc;
       l += 1;
     }
   }
@@ -308,6 +393,9 @@ void release(rl_decode_driver* v) {
     if (g) (void)hipGraphExecDestroy(g);
   for (auto g : v->single_pf)
     if (g) (void)hipGraphExecDestroy(g);
+  if (v->first_pf) (void)hipGraphExecDestroy(v->first_pf);
+  if (v->ev_done) (void)hipEventDestroy(v->ev_done);
+
   for (auto g : v->graphs) (void)hipGraphDestroy(g);
   if (v->dev) (void)hipFree(v->dev);
   if (v->host) (void)hipHostFree(v->host);
@@ -349,6 +437,15 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   v->pool = static_cast<uint8_t*>(c->slot_pool);
   v->store = static_cast<const uint8_t*>(c->host_store);
   v->slot_bytes = rl_slot_bytes(d);
+  {
+    // loads go through the gather kernel when the store has a device address
+    // (pinned by hipHostMalloc); else one hipMemcpyAsync per expert
+    void* p = nullptr;
+    if (v->slot_bytes % 16 == 0 &&
+        hipHostGetDevicePointer(&p, const_cast<void*>(c->host_store), 0) == hipSuccess)
+      v->store_dev = p;
+    (void)hipGetLastError();
+  }
   v->cache = c->cache;
   v->x = c->x;
   const int64_t H = v->H, k = v->k;
@@ -366,9 +463,15 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
                 o_pscr = o_scr + up(v->scratch_bytes), dev_bytes = o_pscr + up(v->pscratch_bytes);
   const int64_t h_flags = 0, h_miss = h_flags + 4 * L, h_ids = h_miss + 4 * L,
                 h_pids = h_ids + 4 * L * k, h_pairs = up(h_pids + 4 * k),
-                h_table = h_pairs + up(4 * 4 * k), host_bytes = h_table + up(4 * int64_t(L) * v->E);
+                h_table = h_pairs + up(4 * 4 * k),
+                host_bytes = h_table + up(4 * int64_t(L) * v->E);
   if (hipMalloc(&v->dev, dev_bytes) != hipSuccess) v->dev = nullptr;
   if (hipHostMalloc(&v->host, host_bytes, hipHostMallocDefault) != hipSuccess) v->host = nullptr;
+  if (hipEventCreateWithFlags(&v->ev_done, hipEventDisableTiming) != hipSuccess) {
+    v->ev_done = nullptr;
+    release(v);
+    return nullptr;
+  }
   if (!v->dev || !v->host) {
     release(v);
     return nullptr;
@@ -395,6 +498,10 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   v->h_ids = reinterpret_cast<int32_t*>(hb + h_ids);
   v->h_pids = reinterpret_cast<int32_t*>(hb + h_pids);
   v->h_pairs = reinterpret_cast<int32_t*>(hb + h_pairs);
+  if (v->prefetch && !v->store_dev) {   // prefetch copies through the gather launch
+    release(v);
+    return nullptr;
+  }
   v->h_table = reinterpret_cast<int32_t*>(hb + h_table);
   int rc = rl_cache_table(v->cache, v->h_table);
   // the device table starts as the cache's table
@@ -403,15 +510,17 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
     rc = RL_E_DEVICE;
   if (!rc && hipMemsetAsync(v->dev, 0, dev_bytes, v->st) != hipSuccess) rc = RL_E_DEVICE;
   // one eager layer (and prediction) before any capture
-  if (!rc) rc = run_body(v, 0, 1, v->prefetch);
+  if (!rc && v->prefetch) rc = run_body(v, 0, 0, true);
+  if (!rc) rc = run_body(v, 0, 1, false);
   if (!rc && hipStreamSynchronize(v->st) != hipSuccess) rc = RL_E_DEVICE;
   v->suffix.assign(L, nullptr);
   v->single.assign(L, nullptr);
-  v->single_pf.assign(v->prefetch ? L - 1 : 0, nullptr);
+  v->single_pf.assign(L, nullptr);
+  if (!rc && v->prefetch) rc = capture(v, 0, 0, true, &v->first_pf);
   for (int l = 0; l < L && !rc; ++l) {
     rc = capture(v, l, L, false, &v->suffix[l]);
     if (!rc) rc = capture(v, l, l + 1, false, &v->single[l]);
-    if (!rc && v->prefetch && l + 1 < L) rc = capture(v, l, l + 1, true, &v->single_pf[l]);
+    if (!rc && v->prefetch && l + 2 < L) rc = capture(v, l, l + 1, true, &v->single_pf[l]);
   }
   if (rc) {
     release(v);

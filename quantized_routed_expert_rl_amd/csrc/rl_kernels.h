@@ -52,6 +52,10 @@ struct DecodeArgs {
   float* x_out = nullptr;
   float* a_out = nullptr;
   float eps = 0.f;
+  // words the router kernel zeroes first (a one-token rl_route's miss count
+  // and flag, which its top-k kernel then accumulates), or NULL
+  uint32_t* clear_miss = nullptr;
+  uint32_t* clear_flag = nullptr;
 };
 void launch_decode_router(const DecodeArgs& a, hipStream_t st);
 void launch_decode_gateup(const DecodeArgs& a, hipStream_t st);
@@ -123,5 +127,19 @@ void launch_residual_add(int T, int H, float* x, const float* y, const uint32_t*
                          hipStream_t st);
 void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st);
 void launch_table_scatter(int32_t* table, const int32_t* pairs, int n, hipStream_t st);
+
+// One layer's expert loads (k <= 32), passed by value to the gather kernel:
+// expert i goes from host-store row src_row[i] to pool slot dst_slot[i];
+// pairs[2j], pairs[2j+1] = (key, slot) residency entries to write, j < n_pairs.
+struct ExpertLoads {
+  int32_t n = 0, n_pairs = 0;
+  int64_t src_row[32];
+  int32_t dst_slot[32];
+  int32_t pairs[128];
+};
+// store_dev: the device address of the pinned host store; slot_bytes % 16 == 0.
+void launch_expert_gather(const void* store_dev, void* pool, int64_t slot_bytes,
+                          const ExpertLoads& ld, int32_t* table, hipStream_t st);
+
 
 }  // namespace rl

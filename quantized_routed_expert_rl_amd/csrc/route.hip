@@ -189,10 +189,29 @@ int cand_per_lane(int E) {
   return n;
 }
 
+// One token: the decode router GEMV (one wave per row, float64 sums, 4 us at
+// E = 512, H = 2048) instead of the GEMM, whose 32-token tiles would be 1/32
+// used (26 us).
 void launch_route(const RouteArgs& a, hipStream_t st) {
-  dim3 grid((a.E + 31) / 32, (a.T + 31) / 32);
-  route_gemm_kernel<<<grid, 512, 0, st>>>(a.x, a.W, a.bias, a.T, a.E, a.H, a.logits,
-                                          a.logits_out, a.miss_count, a.early_out);
+  if (a.T == 1) {
+    DecodeArgs da;
+    da.x = a.x;
+    da.W = a.W;
+    da.bias = a.bias;
+    da.E = a.E;
+    da.H = a.H;
+    da.logits = a.logits;
+    da.logits_out = a.logits_out;
+    da.early_out = a.early_out;
+    da.sticky = false;
+    da.clear_miss = a.miss_count;
+    da.clear_flag = a.early_out;
+    launch_decode_router(da, st);
+  } else {
+    dim3 grid((a.E + 31) / 32, (a.T + 31) / 32);
+    route_gemm_kernel<<<grid, 512, 0, st>>>(a.x, a.W, a.bias, a.T, a.E, a.H, a.logits,
+                                            a.logits_out, a.miss_count, a.early_out);
+  }
   switch (cand_per_lane(a.E)) {
     case 1: launch_topk_n<1>(a, st); break;
     case 2: launch_topk_n<2>(a, st); break;

@@ -145,6 +145,48 @@ void launch_table_scatter(int32_t* table, const int32_t* pairs, int n, hipStream
   table_scatter_kernel<<<1, 64, 0, st>>>(table, pairs, n);
 }
 
+// One layer's expert loads in one launch: expert e (blockIdx.y) is copied
+// from row src_row[e] of the host store, read through its device address
+// (pinned host memory, over PCIe), into pool slot dst_slot[e]; block (0, 0)
+// also writes the residency entries the loads change.  Every block keeps
+// four 16-byte reads in flight per thread.
+__global__ __launch_bounds__(256) void expert_gather_kernel(const uint4* __restrict__ store,
+                                                            uint4* __restrict__ pool,
+                                                            int64_t slot_vecs, ExpertLoads ld,
+                                                            int32_t* __restrict__ table) {
+  const int e = blockIdx.y;
+  const uint4* src = store + ld.src_row[e] * slot_vecs;
+  uint4* dst = pool + int64_t(ld.dst_slot[e]) * slot_vecs;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i0 = int64_t(blockIdx.x) * 256 + threadIdx.x; i0 < slot_vecs; i0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * stride < slot_vecs) v[u] = src[i0 + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * stride < slot_vecs) dst[i0 + u * stride] = v[u];
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < ld.n_pairs; i += 256) table[ld.pairs[2 * i]] = ld.pairs[2 * i + 1];
+}
+
+void launch_expert_gather(const void* store_dev, void* pool, int64_t slot_bytes,
+                          const ExpertLoads& ld, int32_t* table, hipStream_t st) {
+  if (ld.n <= 0 && ld.n_pairs <= 0) return;
+  const dim3 grid(64, ld.n > 0 ? ld.n : 1);
+  ExpertLoads a = ld;
+  if (a.n <= 0) {                      // entries only: one block, no copy
+    a.src_row[0] = 0;
+    a.dst_slot[0] = 0;
+    expert_gather_kernel<<<dim3(1, 1), 256, 0, st>>>(static_cast<const uint4*>(store_dev),
+                                                      static_cast<uint4*>(pool), 0, a, table);
+    return;
+  }
+  expert_gather_kernel<<<grid, 256, 0, st>>>(static_cast<const uint4*>(store_dev),
+                                             static_cast<uint4*>(pool), slot_bytes / 16, a, table);
+}
+
 void launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, hipStream_t st) {
   stream_read_kernel<<<8 * n_cu, 256, 0, st>>>(static_cast<const uint4*>(buf), bytes / 16, sink);
 }

@@ -177,12 +177,15 @@ class ServicedDecodeStack:
     output equals that of a fully resident stack.
 
     ``prefetch`` adds the notes' pre-gated prefetch to the synchronous path
-    ("Red Lite dev23", "What changed", pre-gated prefetch): layer l+1's router
-    applied to layer l's input predicts layer l+1's selection (rl_route into
-    buffers of its own, in layer l's graph, so no layer flag is touched);
-    after layer l the host reserves the predicted experts in the cache and
-    queues their copies ahead of layer l+1, which then finds most of its
-    misses resident.
+    ("Red Lite dev23", "What changed", pre-gated prefetch): layer m's router
+    applied to layer m-1's input predicts layer m's selection (rl_route into
+    buffers of its own, so no layer flag is touched).  Layer l's graph ends
+    with layer l+1's input, so it also predicts layer l+2; after layer l the
+    host reserves the predicted experts in the cache with no victim among
+    layer l+1's slots and queues their copies ahead of layer l+2 (layer 1 is
+    predicted from layer 0's input before layer 0).  This is the order of the
+    native driver, whose copies run on a stream of their own while layer l+1
+    runs, so the cache decisions of the two agree step for step.
     ``stats`` counts the predictions and how many predicted experts layer
     l+1 then selected (the accuracy the notes did not measure).
 
@@ -234,9 +237,11 @@ class ServicedDecodeStack:
         self.stream = torch.cuda.Stream()
         self.suffix = [self._capture(l, self.L) for l in range(self.L)]
         self.single = [self._capture(l, l + 1) for l in range(self.L)]
-        # layer l with the prediction of layer l+1's selection in the same graph
-        self.single_pf = ([self._capture(l, l + 1, predict=True) for l in range(self.L - 1)]
+        # layer l, then the prediction of layer l+2's selection from layer l+1's
+        # input; and layer 1's prediction from layer 0's input
+        self.single_pf = ([self._capture(l, l + 1, predict=True) for l in range(self.L - 2)]
                           if prefetch else [])
+        self.first_pf = self._capture(0, 0, predict=True) if prefetch and self.L > 1 else None
 
     def _predict(self, l):
         """Layer l+1's router on layer l's input, into the prediction buffers."""
@@ -249,21 +254,27 @@ class ServicedDecodeStack:
                               s.a[l + 1], EPS)
 
     def _capture(self, l0, l1, predict=False):
+        """Layers l0 .. l1-1, then (predict) layer l1+1's router on layer l1's input."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(self.stream):
             for rep in range(2):              # once to warm up, once captured
                 with (torch.cuda.graph(g, stream=self.stream) if rep else _nullcontext()):
-                    if predict:
-                        self._predict(l0)
                     for l in range(l0, l1):
                         self._layer(l)
+                    if predict:
+                        self._predict(l1)
         return g
 
-    def _load(self, layer, ids, stage):
-        """Reserve layer's ids in the cache and queue the copies of the
-        missing ones (from the pinned rows ``stage``) and the table update on
-        the stream; returns (loads, slots, gens)."""
-        n, slots, load, evicted, gens = self.cache.reserve(layer, ids)
+    def _load(self, layer, ids, stage, exclude_layer=-1):
+        """Reserve layer's ids in the cache (no victim among exclude_layer's
+        experts when >= 0; a reservation refused for want of such slots loads
+        nothing) and queue the copies of the missing ones (from the pinned
+        rows ``stage``) and the table update on the stream; returns (loads,
+        slots, gens)."""
+        n, slots, load, evicted, gens = self.cache.reserve(layer, ids, exclude_layer, raw=True)
+        if n == B.RL_E_RANGE and exclude_layer >= 0:
+            return 0, slots, gens
+        B.check(min(n, 0), "rl_cache_reserve")
         pool = self.model.pool
         for i in np.nonzero(load)[0] if n else ():
             if hasattr(self.source, "row"):      # pinned store: one copy, host to slot
@@ -281,15 +292,17 @@ class ServicedDecodeStack:
         self.cache.commit()
         return n, slots, gens
 
-    def _service(self, f):
-        """Load layer f's missing experts, then run layer f again."""
+    def _service(self, f, graph=None):
+        """Load layer f's missing experts, then run layer f again (``graph``:
+        layer f's graph with the next prediction, recomputed on the finished
+        input)."""
         s = self.stack
         ids = s.routes[f].ids[0].cpu().numpy()
         n, slots, gens = self._load(f, ids, self.stage)
         self.stats["loads"] += n
         if self.sticky:
             self.flags.zero_()
-        self.single[f].replay()
+        (graph or self.single[f]).replay()
         flag = int(self.flags[0 if self.sticky else f].item())
         assert flag == 0, f"layer {f} still misses after its experts were loaded"
         for sl, g in zip(slots, gens):        # no slot of the run was reloaded meanwhile
@@ -323,22 +336,26 @@ class ServicedDecodeStack:
                             break
                         f = l + int(hit[0])
                 else:
-                    predict = self.prefetch and l + 1 < self.L
+                    def prefetch(m):          # queued ahead of layer m; layer m-1 runs first
+                        pids = self.pred.ids[0].cpu().numpy()
+                        predicted[m] = pids
+                        self.stats["prefetch_loads"] += self._load(m, pids, self.pstage,
+                                                                   exclude_layer=m - 1)[0]
+                    if l == 0 and self.first_pf is not None:
+                        self.first_pf.replay()
+                        prefetch(1)
+                    predict = self.prefetch and l + 2 < self.L
+                    g = self.single_pf[l] if predict else self.single[l]
                     if self.sticky:
                         self.flags.zero_()
-                    (self.single_pf if predict else self.single)[l].replay()
-                    # one wait per layer: its flag and the prediction together
+                    g.replay()
                     self.h_flags.copy_(self.flags, non_blocking=True)
-                    if predict:
-                        self.h_pred.copy_(self.pred.ids[0], non_blocking=True)
                     self.stream.synchronize()
                     if int(self.h_flags[0 if self.sticky else l]) != 0:
                         n_eo += 1
-                        self._service(l)
-                    if predict:                       # queued ahead of layer l+1
-                        pids = self.h_pred.numpy().copy()
-                        predicted[l + 1] = pids
-                        self.stats["prefetch_loads"] += self._load(l + 1, pids, self.pstage)[0]
+                        self._service(l, g)
+                    if predict:
+                        prefetch(l + 2)
                     l += 1
                     continue
                 n_eo += 1

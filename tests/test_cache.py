@@ -31,7 +31,7 @@ class ModelLRU:
         self.order.remove(slot)
         self.order.insert(0, slot)
 
-    def reserve(self, layer, ids):
+    def reserve(self, layer, ids, exclude=-1):
         self.stats["reservations"] += 1
         keys = [layer * self.E + int(e) for e in ids]
         saved = (list(self.order), list(self.key_of), dict(self.slot_of))
@@ -40,7 +40,11 @@ class ModelLRU:
         for s in slots:
             if s >= 0 and s not in held:
                 held.append(s)
-        free = [s for s in self.order if s not in held]
+        free = [s for s in self.order if s not in held
+                and (self.key_of[s] < 0 or self.key_of[s] // self.E != exclude)]
+        if len({k for k, s in zip(keys, slots) if s < 0}) > len(free):
+            self.stats["aborts"] += 1            # refused before anything changes
+            return None
         load, evicted = [0] * len(keys), [-1] * len(keys)
         for i, k in enumerate(keys):
             if slots[i] >= 0:
@@ -108,8 +112,14 @@ def test_cache_matches_model(n_slots, L, E, k, seed):
         layer = int(rng.integers(L))
         p = 1.0 / (np.arange(E) + 1.0) ** 1.1
         ids = pop[rng.choice(E, k, replace=False, p=p / p.sum())].astype(np.int32)
-        got = c.reserve(layer, ids)
-        want = m.reserve(layer, ids)
+        # a third of the reservations exclude another layer's slots as victims
+        excl = int(rng.integers(L)) if rng.random() < 0.33 else -1
+        got = c.reserve(layer, ids, exclude_layer=excl, raw=True)
+        want = m.reserve(layer, ids, excl)
+        if want is None:                         # too few slots qualify: refused, unchanged
+            assert got[0] == B.RL_E_RANGE, step
+            assert np.array_equal(c.table(), m.table(L)), step
+            continue
         assert got[0] == want[0]
         for a, b in zip(got[1:], want[1:]):
             assert list(a) == list(b), step
@@ -152,6 +162,28 @@ def test_selection_larger_than_the_pool_is_refused_and_rolled_back():
     assert c.stats()["aborts"] == 1
     n, *_ = c.reserve(0, [1, 3])                 # the cache is usable afterwards
     assert n == 1
+    c.commit()
+
+
+def test_excluded_layer_keeps_its_slots():
+    # 4 slots: layer 0 holds experts 1, 2 (least recent), layer 1 holds 3, 4;
+    # a layer-2 reservation that excludes layer 0 must evict layer 1's slots
+    c = B.ExpertCache(4, 3, 8)
+    for s, (l, e) in enumerate([(0, 1), (0, 2), (1, 3), (1, 4)]):
+        c.insert(l, e, s)
+    n, slots, load, evicted, gens = c.reserve(2, [5, 6], exclude_layer=0)
+    assert n == 2 and sorted(slots.tolist()) == [2, 3]
+    assert sorted(evicted.tolist()) == [1 * 8 + 3, 1 * 8 + 4]
+    c.commit()
+    assert c.lookup(0, 1) == 0 and c.lookup(0, 2) == 1
+    # three misses, only the two layer-2 slots... all remaining victims are
+    # layer 0's or the selection's own: refused, nothing changes
+    before = c.table().copy()
+    n, *_ = c.reserve(1, [0, 1, 2], exclude_layer=0, raw=True)
+    assert n == B.RL_E_RANGE and np.array_equal(c.table(), before)
+    # without the exclusion the same reservation evicts layer 0's experts
+    n, slots, load, evicted, gens = c.reserve(1, [0, 1], exclude_layer=-1)
+    assert n == 2 and sorted(evicted.tolist()) == [1, 2]
     c.commit()
 
 
