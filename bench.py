@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--stacks", action="store_true",
                     help="also time prefill_48l with 3-bit weights and the bounded-pool decode stacks "
                          "(miss service, prefetch, native driver)")
+    ap.add_argument("--slope", action="store_true",
+                    help="only the decode expert stages against top_k = 1..k (warm and cache-flushed) "
+                         "with a line fitted per stage, as one JSON line; nothing else runs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -90,6 +93,100 @@ def event_ms(fn, stream, reps):
     return s.elapsed_time(e) / reps
 
 
+def cold_ms(items, flush, stream, reps=5):
+    """Milliseconds per item with the Infinity Cache flushed before each: a
+    graph of (flush, item) pairs and a graph of the flushes alone, replayed
+    reps times each; the difference of their medians over the item count."""
+    import torch
+
+    def cap(with_items):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for it in items:
+                flush.add_(1.0)
+                if with_items:
+                    it()
+        g.replay()
+        return g
+    gp, gf = cap(True), cap(False)
+    tp, tf = [], []
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            tp.append(event_ms(gp.replay, stream, 1))
+            tf.append(event_ms(gf.replay, stream, 1))
+    del gp, gf
+    return (sorted(tp)[reps // 2] - sorted(tf)[reps // 2]) / len(items)
+
+
+def slope(args, model, X, stream):
+    """Decode expert stages against top_k = 1 .. k of the same layer (same
+    router, pool and tokens; only the descriptor's top_k changes): warm time
+    per launch over a graph of T launches, cold time by cold_ms over 32, and a
+    least-squares line t = a + b*k per stage, so the per-expert streaming
+    cost b separates from the fixed latency a."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    from quantized_routed_expert_rl_amd import binding as B
+    from quantized_routed_expert_rl_amd.device import RouteBuffers
+
+    w, lib = model.w, B.lib
+    T = min(args.tokens, 128)
+    flush = torch.zeros(512 << 18, device="cuda")
+    W0, res, pool = model.router[0].data_ptr(), model.residency.data_ptr(), model.pool.data_ptr()
+    tb = B.rl_tensor_bytes(model.desc)
+    rows = []
+    for k in range(1, w.top_k + 1):
+        dk = B.desc(w.hidden, w.n_experts, k, w.width, 1, w.qbits, model.desc.n_slots)
+        sbk = B.rl_decode_scratch_bytes(dk)
+        scr = torch.zeros(T, sbk, dtype=torch.uint8, device="cuda")
+        rb = RouteBuffers.alloc(T, k, w.n_experts, with_logits=False)
+        mc = torch.zeros(T, dtype=torch.int32, device="cuda")     # per token: calls stay independent
+        eo = torch.zeros(T, dtype=torch.int32, device="cuda")
+        outs = [B.route_out(rb.ids[t], rb.weights[t], rb.slots[t], mc[t:t + 1], eo[t:t + 1])
+                for t in range(T)]
+        Y = torch.empty(T, w.hidden, device="cuda")
+
+        def stage(sg, t, dk=dk, scr=scr, outs=outs, Y=Y, sbk=sbk):
+            return lambda: lib.rl_decode_stage(C.byref(dk), sg, 0, X[t].data_ptr(), W0, None, res,
+                                               pool, C.byref(outs[t]), scr[t].data_ptr(), sbk,
+                                               Y[t].data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream)
+        with torch.cuda.stream(stream):
+            for t in range(T):
+                for sg in (0, 1, 2):
+                    assert stage(sg, t)() == 0
+        stream.synchronize()
+        row = {"k": k}
+        for sg, name in ((1, "gateup"), (2, "down")):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(T):
+                    stage(sg, t)()
+            g.replay()
+            with torch.cuda.stream(stream):
+                row[name + "_us"] = round(event_ms(g.replay, stream, 5) * 1e3 / T, 3)
+                row[name + "_cold_us"] = round(
+                    cold_ms([stage(sg, t) for t in range(32)], flush, stream) * 1e3, 3)
+            del g
+        assert int(mc.sum().cpu()) == 0 and int(eo.sum().cpu()) == 0
+        rows.append(row)
+        del scr, rb, mc, eo, outs, Y
+    ks = np.array([r["k"] for r in rows], float)
+    fits = {}
+    for name, per_expert in (("gateup", 2 * tb), ("down", tb)):
+        for kind in ("", "_cold"):
+            b, a = np.polyfit(ks, [r[name + kind + "_us"] for r in rows], 1)
+            fits[name + kind] = {"intercept_us": round(float(a), 3),
+                                 "us_per_expert": round(float(b), 4),
+                                 "expert_bytes": int(per_expert),
+                                 "gbs_per_expert_slope": round(per_expert / (b * 1e-6) / 1e9, 1)}
+    print(json.dumps({"mode": "slope", "workload": f"decode_1l, top_k 1..{w.top_k}, {T} tokens",
+                      "rows": rows, "fits": fits}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -121,6 +218,9 @@ def main():
     model = DeviceModel(w)
     T = args.tokens
     X = to_dev(synth.activations(w, T, stream=1))
+    if args.slope:
+        slope(args, model, X, stream)
+        return
     Y = torch.empty(T, w.hidden, device="cuda")
     rb = RouteBuffers.alloc(T, w.top_k, w.n_experts, with_logits=False)
     outs = [B.route_out(rb.ids[t], rb.weights[t], rb.slots[t], rb.miss_count, rb.early_out)
@@ -213,23 +313,7 @@ def main():
     flush = None if args.no_cold else torch.zeros(512 << 18, device="cuda")
 
     def cold_per_item_ms(items, reps=5):
-        def cap(with_items):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for it in items:
-                    flush.add_(1.0)
-                    if with_items:
-                        it()
-            g.replay()
-            return g
-        gp, gf = cap(True), cap(False)
-        tp, tf = [], []
-        for _ in range(reps):
-            with torch.cuda.stream(stream):
-                tp.append(event_ms(gp.replay, stream, 1))
-                tf.append(event_ms(gf.replay, stream, 1))
-        del gp, gf
-        return (sorted(tp)[reps // 2] - sorted(tf)[reps // 2]) / len(items)
+        return cold_ms(items, flush, stream, reps)
 
     gu_cold_ms = None
     if flush is not None:

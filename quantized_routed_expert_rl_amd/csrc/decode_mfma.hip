@@ -125,8 +125,8 @@ __device__ __forceinline__ void quantize_loaded(const float* v, int run, bool ac
 // renormalised weights and writes ids, weights, slots, the miss count and
 // the flag; a work block only needs its slots.  Work block = (rank r, 4*RPT rows j); wave w takes
 // RPT rows of gate and up over all KB = H/256 K-blocks: 2*NH diagonal tiles.
-template <int N, int KB, int QBITS>
-__global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
+template <int N, int KB, int QBITS, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_topk_gateup_mfma_kernel(
     PoolView pv, int H, int F, int E, int k, int layer, int n_slots,
     const float* __restrict__ x, const float* __restrict__ logits,
     const int32_t* __restrict__ residency, int32_t* ids, float* weights, int32_t* slots,
@@ -161,15 +161,18 @@ __global__ __launch_bounds__(256) void decode_topk_gateup_mfma_kernel(
       if (lane == 0) s_miss = miss;
     }
   } else if (!publisher) {
-    const int run = tid - 64;            // H/16 <= 128 runs over waves 1-2
-    float v[16];
-    load_run(x, run, run < H / 16, v);
-    quantize_loaded(v, run, run < H / 16, s_xq, s_xe);
+    // H/16 <= 128 runs over waves 1-2 (wave 1 alone takes two per lane when
+    // the block has two waves); a wave's runs are all below 128 or all above
+    for (int run = tid - 64; run < 128; run += 64 * (NW > 2 ? 2 : 1)) {
+      float v[16];
+      load_run(x, run, run < H / 16, v);
+      quantize_loaded(v, run, run < H / 16, s_xq, s_xe);
+    }
   }
   if (publisher) return;
   __syncthreads();
   if (s_miss) return;                    // early-out: nothing downstream runs
-  const int jpb = 4 * RPT;
+  const int jpb = NW * RPT;
   const int bpr = F / jpb;
   const int r = blockIdx.x / bpr;
   const int j0 = (blockIdx.x % bpr) * jpb + wv * RPT;
@@ -310,11 +313,17 @@ __global__ __launch_bounds__(1024) void decode_down_sum_mfma_kernel(
 }
 
 // ------------------------------------------------------------ launchers
+// Waves per gate/up block (4 rows each at H = 2048).  At the real shape four
+// waves give 321 blocks on 256 compute units; two waves (641 blocks) and
+// sixteen (81) were slower, eight (161) the same (measured per launch: 6.32,
+// 7.07 and 6.05 against 5.97 us).
+constexpr int kGateupWaves = 4;
+
 template <int N, int KB, int QBITS>
 static void gateup_mfma(const DecodeArgs& a, hipStream_t st) {
   constexpr int BPT = KB < 4 ? KB : 4;
-  const int blocks = a.k * (a.F / (4 * (16 / BPT))) + 1;
-  decode_topk_gateup_mfma_kernel<N, KB, QBITS><<<blocks, 256, 0, st>>>(
+  const int blocks = a.k * (a.F / (kGateupWaves * (16 / BPT))) + 1;
+  decode_topk_gateup_mfma_kernel<N, KB, QBITS, kGateupWaves><<<blocks, 64 * kGateupWaves, 0, st>>>(
       a.pool, a.H, a.F, a.E, a.k, a.layer, a.n_slots, a.x, a.logits, a.residency, a.ids,
       a.weights, a.slots, a.miss_count, a.early_out, a.hbuf, int(a.sticky));
 }
