@@ -41,10 +41,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="no HIP graph for the decode step")
     ap.add_argument("--no-stacks", action="store_true",
-                    help="skip the 48-layer stacks of the default line (decode_48l, prefill_48l 2-bit)")
+                    help="skip the 48-layer stacks of the default line (decode_48l, prefill_48l 2-bit, "
+                         "the bounded-pool decode by the native driver with and without prefetch)")
     ap.add_argument("--stacks", action="store_true",
-                    help="also time prefill_48l with 3-bit weights and the bounded-pool decode stacks "
-                         "(miss service, prefetch, native driver)")
+                    help="also time prefill_48l with 3-bit weights and the other bounded-pool decode "
+                         "variants (Python loop, early-out path, sticky flag)")
     ap.add_argument("--slope", action="store_true",
                     help="only the decode expert stages against top_k = 1..k (warm and cache-flushed) "
                          "with a line fitted per stage, as one JSON line; nothing else runs")
@@ -568,20 +569,23 @@ def main():
                             f"Zipf-biased routing, all experts resident, {qb}-bit block weights"}
             del mp_, ps
             torch.cuda.empty_cache()
-    if args.stacks:
+    if args.stacks or not args.no_stacks:
         # decode with a bounded pool (each layer's 224 most popular experts
-        # resident) and miss service, without and with the pre-gated prefetch
+        # resident) and miss service, without and with the pre-gated prefetch:
+        # the native driver on the default line, the Python loop and the
+        # early-out-path variants with --stacks
         from quantized_routed_expert_rl_amd.stack import (HostExpertStore, NativeServicedDecode,
                                                           ServicedDecodeStack)
         wh = workloads.get("decode_48l_hot")
         store = HostExpertStore(wh)
         Xh = to_dev(synth.activations(wh, wh.tokens))
-        runs = [("", dict()), ("_prefetch", dict(prefetch=True)),
-                ("_early_out_path", dict(early_out_limit=1 << 30)),
-                ("_early_out_path_sticky", dict(early_out_limit=1 << 30, sticky=True)),
-                ("_native", dict(native=True)), ("_native_prefetch", dict(native=True, prefetch=True)),
-                ("_native_early_out_path_sticky",
-                 dict(native=True, early_out_limit=1 << 30, sticky=True))]
+        runs = [("_native", dict(native=True)), ("_native_prefetch", dict(native=True, prefetch=True))]
+        if args.stacks:
+            runs += [("", dict()), ("_prefetch", dict(prefetch=True)),
+                     ("_early_out_path", dict(early_out_limit=1 << 30)),
+                     ("_early_out_path_sticky", dict(early_out_limit=1 << 30, sticky=True)),
+                     ("_native_early_out_path_sticky",
+                      dict(native=True, early_out_limit=1 << 30, sticky=True))]
         for tag, kw in runs:
             mh = DeviceModel(wh, pool=store.device_pool(synth.residency(wh)))
             kw = dict(kw)

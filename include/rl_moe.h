@@ -370,9 +370,10 @@ int rl_cache_stats(const rl_cache* c, int64_t* out);
  * after a token every layer's selection is touched in the cache ("Red Lite
  * dev21", "What changed", LRU stamps refreshed after the token).  With
  * prefetch, layer l's graph also runs layer l+2's router on layer l+1's
- * input; the host reserves those experts (no victim among layer l+1's slots)
- * and their gather is queued right behind layer l+1's graph, so the copies
- * run while the host reads layer l+1's flags and relaunches.
+ * input (in the step between the layers), the host takes the top k of those
+ * logits, reserves the experts (no victim among layer l+1's slots), and
+ * their gather is queued right behind layer l+1's graph, so the copies run
+ * while the host reads layer l+1's flags and relaunches.
  *
  * rl_driver_config (host struct; the pointers stay owned by the caller and
  * must outlive the driver):

@@ -48,6 +48,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -56,7 +57,6 @@
 
 struct rl_decode_driver {
   rl_moe_desc d;          // as given (flags may hold RL_STICKY_EARLY_OUT)
-  rl_moe_desc dr;         // without flags: the prediction's rl_route
   int L = 0, E = 0, H = 0, k = 0;
   bool sticky = false, prefetch = false, sync_path = false;
   int limit = 0;
@@ -74,15 +74,16 @@ struct rl_decode_driver {
   // device buffers (one allocation)
   void* dev = nullptr;
   float *a = nullptr, *y = nullptr;
-  int32_t *ids = nullptr, *slots = nullptr, *pids = nullptr, *pslots = nullptr;
-  float *wts = nullptr, *pw = nullptr;
-  uint32_t *miss = nullptr, *flags = nullptr, *pmiss = nullptr, *pflag = nullptr;
-  uint8_t *scratch = nullptr, *pscratch = nullptr;
-  int64_t scratch_bytes = 0, pscratch_bytes = 0;
+  int32_t *ids = nullptr, *slots = nullptr;
+  float *wts = nullptr, *plogits = nullptr;   // plogits: the prediction's router logits [E]
+  uint32_t *miss = nullptr, *flags = nullptr, *pflag = nullptr;
+  uint8_t* scratch = nullptr;
+  int64_t scratch_bytes = 0;
   // pinned host mirrors and the host copy of the residency table
   void* host = nullptr;
   uint32_t *h_flags = nullptr, *h_miss = nullptr;
-  int32_t *h_ids = nullptr, *h_pids = nullptr, *h_table = nullptr;
+  int32_t *h_ids = nullptr, *h_table = nullptr;
+  float* h_plogits = nullptr;
   int32_t *h_pairs = nullptr, *d_pairs = nullptr;   // changed table entries (key, slot)
   rl::ExpertLoads pf;                 // prefetch loads for the next gather launch
   std::vector<hipGraph_t> graphs;
@@ -107,45 +108,85 @@ rl_route_out layer_route(const rl_decode_driver* v, int l) {
   return o;
 }
 
-int run_layer(rl_decode_driver* v, int l) {
+// Layer l, then the step to layer l+1 (x_{l+1}, a_{l+1}).  With predict that
+// step is the library's fused residual + norm + router kernel run with layer
+// l+2's router: a_{l+1} bit for bit as rl_residual_rmsnorm gives it, and the
+// prediction's logits as the router GEMV gives them, in one launch.
+int run_layer(rl_decode_driver* v, int l, bool predict) {
   const rl_route_out o = layer_route(v, l);
-  int rc = moe_decode_layer(&v->d, l, v->a + int64_t(l) * v->H, v->W[l], v->bias[l], v->residency,
-                            v->pool, &o, v->scratch, v->scratch_bytes, v->y + int64_t(l) * v->H,
-                            v->st);
+  const int64_t H = v->H;
+  int rc = moe_decode_layer(&v->d, l, v->a + l * H, v->W[l], v->bias[l], v->residency, v->pool, &o,
+                            v->scratch, v->scratch_bytes, v->y + l * H, v->st);
   if (rc) return rc;
-  return rl_residual_rmsnorm(1, v->H, v->x + int64_t(l) * v->H, v->y + int64_t(l) * v->H,
-                             o.early_out, v->x + int64_t(l + 1) * v->H,
-                             v->a + int64_t(l + 1) * v->H, v->eps, v->st);
+  if (!predict)
+    return rl_residual_rmsnorm(1, v->H, v->x + l * H, v->y + l * H, o.early_out,
+                               v->x + (l + 1) * H, v->a + (l + 1) * H, v->eps, v->st);
+  rl::DecodeArgs a{};
+  a.x_prev = v->x + l * H;
+  a.y_prev = v->y + l * H;
+  a.flag_prev = o.early_out;
+  a.x_out = v->x + (l + 1) * H;
+  a.a_out = v->a + (l + 1) * H;
+  a.eps = v->eps;
+  a.W = v->W[l + 2];
+  a.bias = v->bias[l + 2];
+  a.E = v->E;
+  a.H = v->H;
+  a.logits = v->plogits;
+  a.early_out = v->pflag;               // not read: no sticky flag here
+  a.sticky = false;
+  rl::launch_decode_router(a, v->st);
+  return hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVICE;
 }
 
-// layer l+1's router on layer l's input, into the prediction buffers
+// layer l+1's router on a_l alone (a token's first prediction)
 int run_predict(rl_decode_driver* v, int l) {
-  rl_route_out o;
-  o.ids = v->pids;
-  o.weights = v->pw;
-  o.slots = v->pslots;
-  o.miss_count = v->pmiss;
-  o.early_out = v->pflag;
-  o.logits = nullptr;
-  return rl_route(&v->dr, l + 1, 1, v->a + int64_t(l) * v->H, v->W[l + 1], v->bias[l + 1],
-                  v->residency, &o, v->pscratch, v->pscratch_bytes, v->st);
+  rl::DecodeArgs a{};
+  a.x = v->a + int64_t(l) * v->H;
+  a.W = v->W[l + 1];
+  a.bias = v->bias[l + 1];
+  a.E = v->E;
+  a.H = v->H;
+  a.logits = v->plogits;
+  a.early_out = v->pflag;
+  a.sticky = false;
+  rl::launch_decode_router(a, v->st);
+  return hipGetLastError() == hipSuccess ? RL_OK : RL_E_DEVICE;
 }
 
-// flags [L], miss counts [L], ids [L x k] and predicted ids [k] sit back to
-// back on the device and in the pinned mirror: one copy moves them all
+// The first k experts of the order (logit descending, index ascending) on the
+// host, with the routing kernels' key (-0 as +0, a total order on the bits).
+void host_topk(const float* lg, int E, int k, int32_t* ids) {
+  std::vector<uint32_t> key(E);
+  for (int e = 0; e < E; ++e) {
+    const float f = lg[e] + 0.0f;
+    uint32_t u;
+    std::memcpy(&u, &f, sizeof(u));
+    key[e] = u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+  }
+  std::vector<int32_t> idx(E);
+  for (int e = 0; e < E; ++e) idx[e] = e;
+  std::partial_sort(idx.begin(), idx.begin() + k, idx.end(), [&](int32_t a, int32_t b) {
+    return key[a] > key[b] || (key[a] == key[b] && a < b);
+  });
+  for (int i = 0; i < k; ++i) ids[i] = idx[i];
+}
+
+// flags [L], miss counts [L], ids [L x k] and the prediction's logits [E] sit
+// back to back on the device and in the pinned mirror: one copy moves them all
 int run_mirror(rl_decode_driver* v) {
-  const size_t n = sizeof(int32_t) * (2 * v->L + (v->L + 1) * v->k);
+  const size_t n = sizeof(int32_t) * (2 * v->L + v->L * v->k) + sizeof(float) * v->E;
   return hipMemcpyAsync(v->h_flags, v->flags, n, hipMemcpyDeviceToHost, v->st) == hipSuccess
              ? RL_OK
              : RL_E_DEVICE;
 }
 
-// Layers l0 .. l1-1, then (predict) layer l1+1's router on a_{l1}, then the
+// Layers l0 .. l1-1, with (predict) layer l1+1's router on a_{l1}, then the
 // mirror copy.
 int run_body(rl_decode_driver* v, int l0, int l1, bool predict) {
   int rc = RL_OK;
-  for (int l = l0; l < l1 && !rc; ++l) rc = run_layer(v, l);
-  if (!rc && predict) rc = run_predict(v, l1);
+  for (int l = l0; l < l1 && !rc; ++l) rc = run_layer(v, l, predict && l == l1 - 1);
+  if (!rc && predict && l0 == l1) rc = run_predict(v, l1);
   return rc ? rc : run_mirror(v);
 }
 
@@ -330,7 +371,8 @@ int token(rl_decode_driver* v, const float* x0) {
     } else {
       // the predicted experts of layer m, copied behind layer m-1's graph
       auto prefetch = [&](int m) {
-        std::vector<int32_t> p(v->h_pids, v->h_pids + k);
+        std::vector<int32_t> p(k);
+        host_topk(v->h_plogits, v->E, k, p.data());
         const int n = prefetch_layer(v, m, p.data());
         if (n < 0) return n;
         v->stats[7] += n;
@@ -418,8 +460,6 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   rl_decode_driver* v = new (std::nothrow) rl_decode_driver;
   if (!v) return nullptr;
   v->d = *d;
-  v->dr = *d;
-  v->dr.flags = 0;
   v->L = L;
   v->E = d->n_experts;
   v->H = d->hidden;
@@ -450,19 +490,17 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   v->x = c->x;
   const int64_t H = v->H, k = v->k;
   v->scratch_bytes = rl_decode_scratch_bytes(d);
-  v->pscratch_bytes = rl_route_scratch_bytes(&v->dr, 1);
   // one device allocation, every part 256-byte aligned
   auto up = [](int64_t n) { return (n + 255) & ~int64_t(255); };
-  // flags, miss, ids, pids contiguous (one mirror copy)
+  // flags, miss, ids, prediction logits contiguous (one mirror copy)
   const int64_t o_a = 0, o_y = o_a + up(4 * (L + 1) * H), o_flags = o_y + up(4 * L * H),
-                o_miss = o_flags + 4 * L, o_ids = o_miss + 4 * L, o_pids = o_ids + 4 * L * k,
-                o_slots = o_flags + up(4 * (2 * L + (L + 1) * k)),
-                o_wts = o_slots + up(4 * L * k), o_pslots = o_wts + up(4 * L * k),
-                o_pw = o_pslots + up(4 * k), o_pmiss = o_pw + up(4 * k), o_pflag = o_pmiss + 256,
+                o_miss = o_flags + 4 * L, o_ids = o_miss + 4 * L, o_plog = o_ids + 4 * L * k,
+                o_slots = o_flags + up(4 * (2 * L + L * k) + 4 * int64_t(v->E)),
+                o_wts = o_slots + up(4 * L * k), o_pflag = o_wts + up(4 * L * k),
                 o_pairs = o_pflag + 256, o_scr = o_pairs + up(4 * 4 * k),
-                o_pscr = o_scr + up(v->scratch_bytes), dev_bytes = o_pscr + up(v->pscratch_bytes);
+                dev_bytes = o_scr + up(v->scratch_bytes);
   const int64_t h_flags = 0, h_miss = h_flags + 4 * L, h_ids = h_miss + 4 * L,
-                h_pids = h_ids + 4 * L * k, h_pairs = up(h_pids + 4 * k),
+                h_plog = h_ids + 4 * L * k, h_pairs = up(h_plog + 4 * int64_t(v->E)),
                 h_table = h_pairs + up(4 * 4 * k),
                 host_bytes = h_table + up(4 * int64_t(L) * v->E);
   if (hipMalloc(&v->dev, dev_bytes) != hipSuccess) v->dev = nullptr;
@@ -484,19 +522,15 @@ rl_decode_driver* rl_driver_create(const rl_driver_config* c, void* stream) {
   v->wts = reinterpret_cast<float*>(b + o_wts);
   v->miss = reinterpret_cast<uint32_t*>(b + o_miss);
   v->flags = reinterpret_cast<uint32_t*>(b + o_flags);
-  v->pids = reinterpret_cast<int32_t*>(b + o_pids);
-  v->pslots = reinterpret_cast<int32_t*>(b + o_pslots);
-  v->pw = reinterpret_cast<float*>(b + o_pw);
-  v->pmiss = reinterpret_cast<uint32_t*>(b + o_pmiss);
+  v->plogits = reinterpret_cast<float*>(b + o_plog);
   v->pflag = reinterpret_cast<uint32_t*>(b + o_pflag);
   v->d_pairs = reinterpret_cast<int32_t*>(b + o_pairs);
   v->scratch = b + o_scr;
-  v->pscratch = b + o_pscr;
   uint8_t* hb = static_cast<uint8_t*>(v->host);
   v->h_flags = reinterpret_cast<uint32_t*>(hb + h_flags);
   v->h_miss = reinterpret_cast<uint32_t*>(hb + h_miss);
   v->h_ids = reinterpret_cast<int32_t*>(hb + h_ids);
-  v->h_pids = reinterpret_cast<int32_t*>(hb + h_pids);
+  v->h_plogits = reinterpret_cast<float*>(hb + h_plog);
   v->h_pairs = reinterpret_cast<int32_t*>(hb + h_pairs);
   if (v->prefetch && !v->store_dev) {   // prefetch copies through the gather launch
     release(v);
