@@ -348,7 +348,7 @@ def main():
             "eager_us_per_token": round(eager_ms * 1e3 / T, 3),
         },
         "roofline": {
-            "kernel": ("decode_topk_gateup_mfma_kernel<8, 8, 2>" if w.width % 256 == 0
+            "kernel": ("decode_topk_gateup_mfma_kernel<8, 8, 2, 4>" if w.width % 256 == 0
                        else "decode_topk_gateup_kernel<8, 2, 64>"),
             "bound": "hbm",
             "achieved": round(gu_gbs, 1),
