@@ -389,35 +389,45 @@ __global__ __launch_bounds__(512) void prefill_expert_kernel(
         acc[ct][m] = fmaf(fmaf(float(hi), 65536.f, float(lo)), rs, acc[ct][m]);
       }
     if (kb == KB - 1) {
-      // tile done: the lane holds row c of the tile for tokens 8ct + 2m + h
+      // tile done: the lane holds row c of the tile for tokens 8ct + 2m + h.
+      // Every LDS read of the token tables and every lane exchange is issued
+      // before any result is used, and SwiGLU picks its operands by select,
+      // so the tile's end costs two LDS round trips instead of two per output.
       float v[kc][4];
+      int dst[kc][4];
 #pragma unroll
       for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) v[ct][m] = acc[ct][m] * s_cs[8 * ct + 2 * m + h];
+        for (int m = 0; m < 4; ++m) {
+          v[ct][m] = acc[ct][m] * s_cs[8 * ct + 2 * m + h];
+          dst[ct][m] = s_dst[8 * ct + 2 * m + h];
+        }
       if (GATEUP) {
         // gate lanes (c < 16) finish tokens m = 0, 1 and up lanes m = 2, 3
         const bool gl = c < 16;
         const int j = 16 * tile + (c & 15);
+        float other[kc][2];
+#pragma unroll
+        for (int ct = 0; ct < kc; ++ct)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) other[ct][i] = __shfl_xor(gl ? v[ct][2 + i] : v[ct][i], 16);
 #pragma unroll
         for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const float other = __shfl_xor(gl ? v[ct][2 + i] : v[ct][i], 16);
-            const int m = gl ? i : 2 + i;
-            const float hv = gl ? silu_mul(v[ct][i], other) : silu_mul(other, v[ct][2 + i]);
-            const int dst = s_dst[8 * ct + 2 * m + h];
-            if (dst >= 0) out[int64_t(dst) * F + j] = hv;
+            const float g = gl ? v[ct][i] : other[ct][i];
+            const float u = gl ? other[ct][i] : v[ct][2 + i];
+            const float hv = silu_mul(g, u);
+            const int d = gl ? dst[ct][i] : dst[ct][2 + i];
+            if (d >= 0) out[int64_t(d) * F + j] = hv;
           }
       } else {
         const int i0 = 32 * tile + c;
 #pragma unroll
         for (int ct = 0; ct < kc; ++ct)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int dst = s_dst[8 * ct + 2 * m + h];
-            if (dst >= 0) out[int64_t(dst) * H + i0] = v[ct][m];
-          }
+          for (int m = 0; m < 4; ++m)
+            if (dst[ct][m] >= 0) out[int64_t(dst[ct][m]) * H + i0] = v[ct][m];
       }
     }
     };
