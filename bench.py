@@ -191,7 +191,7 @@ def slope(args, model, X, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
               "no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import ctypes as C
