@@ -5,7 +5,7 @@ import torch
 
 from gpu.common import HostInputs, check_route, close, oracle_decode_many, oracle_route, shape_of
 from oracle import moe_oracle as O
-from quantized_routed_expert_rl_amd import synth, workloads
+from quantized_routed_expert_rl_amd import binding as B, synth, workloads
 from quantized_routed_expert_rl_amd.device import DeviceModel, RouteBuffers, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -48,12 +48,39 @@ def test_route_tiny_gemv_and_gemm(tiny):
     w = tiny.w
     x = synth.activations(w, 4)
     ref = oracle_route(tiny, 0, x)
-    for T in (1, 4):     # T=1 takes the GEMV + last-block path, T=4 the GEMM path
+    for T in (1, 4):     # T=1 takes the router GEMV, T=4 the GEMM; both then the top-k kernel
         out = RouteBuffers.alloc(T, w.top_k, w.n_experts)
         scratch = torch.zeros(64 << 10, dtype=torch.uint8, device="cuda")
         tiny.route(0, to_dev(x[:T]), out, scratch)
         check_route(out, oracle_route(tiny, 0, x[:T]))
     assert ref.ids.shape == (4, 2)
+
+
+@pytest.mark.parametrize("table", ["resident", "half"])
+def test_route_one_token_real_shape(real, table):
+    """rl_route with one token at the real shape (router GEMV, then the top-k)
+    against the oracle, with every expert resident and with every second
+    expert missing.  The call zeroes its own miss count and flag, so the
+    values an earlier call left there (7 and 1 here) do not leak in."""
+    w = real.w
+    host = HostInputs.of(real)
+    row = real.table[0].copy()
+    if table == "half":
+        row[1::2] = -1
+    tab = to_dev(row[None, :].astype(np.int32))
+    x = synth.activations(w, 6, stream=3)
+    scratch = torch.zeros(B.rl_route_scratch_bytes(real.desc, 1), dtype=torch.uint8, device="cuda")
+    misses = 0
+    for t in range(x.shape[0]):
+        out = RouteBuffers.alloc(1, w.top_k, w.n_experts)
+        out.miss_count.fill_(7)
+        out.early_out.fill_(1)
+        B.rl_route(real.desc, 0, 1, to_dev(x[t:t + 1]), real.router[0], real.bias[0], tab, out.c(),
+                   scratch, scratch.numel())
+        ref = O.route(x[t:t + 1], host.router(0), host.bias(0), row, w.top_k)
+        check_route(out, ref)
+        misses += ref.miss_count
+    assert (misses > 0) == (table == "half")
 
 
 def test_decode_tiny(tiny):

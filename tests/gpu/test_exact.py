@@ -173,7 +173,8 @@ def test_route_logits_exact(path, T, with_bias):
     rounding of the integer sum, to the last bit ("Red Lite dev23", "What
     changed": the router GEMV in float32 with the sum kept exact), and the
     ids, slots and flags equal the oracle's.  rl_route takes the float64
-    matrix-core GEMM for any token count; a decode call takes the GEMV."""
+    matrix-core GEMM for several tokens and the GEMV for one; a decode call
+    takes the GEMV."""
     H, E, k, F = 2048, 64, 8, 256
     rng = np.random.default_rng(T + 100 * with_bias + 7 * (path == "decode"))
     nw = rng.integers(-64, 65, (E, H))
